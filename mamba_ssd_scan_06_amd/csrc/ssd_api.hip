@@ -1,0 +1,244 @@
+// Host side of libssd: argument checks, workspace layout and the launch
+// sequence of the SSD chunked-scan forward.  The public contract is
+// include/ssd.h.
+//
+// Launch sequence on the caller's stream (each step of the block
+// decomposition in section "SSD算法" of the "Transformers are SSMs" article):
+//   1. chunk_cumsum     dt, A            -> cs           (chunk-local log-decay)
+//   2. chunk_state      x, B, dt, cs     -> states[c]    (green: S_c from a zero start)
+//   3. state_pass       states, cs, h0   -> states[c] := h_{c-1}, final_state (yellow)
+//   4. chunk_output     x, B, C, dt, cs, states, D -> y  (orange + blue + D skip)
+//   5. state_at_index   (only with state_out) -> state_out
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/ssd.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssd_status fail(ssd_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
+    if (!s) return fail(SSD_ERR_NULL, "shape is NULL");
+    if (s->batch < 0 || s->seqlen < 0)
+        return fail(SSD_ERR_SHAPE, "batch (%lld) and seqlen (%lld) must be >= 0", (long long)s->batch,
+                    (long long)s->seqlen);
+    if (s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 || s->ngroups <= 0)
+        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate and ngroups must be > 0");
+    if (s->nheads % s->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "ngroups (%lld) must divide nheads (%lld)", (long long)s->ngroups,
+                    (long long)s->nheads);
+    if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return fail(SSD_ERR_ARGS, "unknown dtype %d", (int)dtype);
+    if (!is_pow2_in(chunk, 8, 256))
+        return fail(SSD_ERR_CHUNK, "chunk_size %d not in {8, 16, 32, 64, 128, 256}", chunk);
+    if (!is_pow2_in(s->headdim, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "headdim %lld not in {16, 32, 64, 128}", (long long)s->headdim);
+    if (!is_pow2_in(s->dstate, 16, 256))
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %lld not in {16, 32, 64, 128, 256}", (long long)s->dstate);
+    if (dtype == SSD_DTYPE_F32 && s->headdim * s->dstate > 128 * 128)
+        return fail(SSD_ERR_UNSUPPORTED, "fp32 inputs need headdim * dstate <= 16384 (LDS budget)");
+    // Index arithmetic inside the kernels: grid dimensions and per-tensor sizes.
+    const int64_t lim = (int64_t)1 << 40;
+    if (s->batch > 65535 || s->nheads > 65535 || s->seqlen > lim / (s->nheads * s->headdim) ||
+        s->batch > lim / ((s->seqlen + 1) * s->nheads * s->headdim))
+        return fail(SSD_ERR_SHAPE, "problem too large");
+    return SSD_OK;
+}
+
+struct Layout {
+    size_t cs_off, st_off, total;
+    int64_t nc;
+};
+
+Layout layout_of(const ssd_shape *s, int chunk) {
+    Layout L;
+    L.nc = (s->seqlen + chunk - 1) / chunk;
+    const size_t cs_bytes = (size_t)s->batch * s->nheads * L.nc * chunk * sizeof(float);
+    const size_t st_bytes = (size_t)s->batch * L.nc * s->nheads * s->headdim * s->dstate * sizeof(float);
+    L.cs_off = 0;
+    L.st_off = round_up(cs_bytes);
+    L.total = L.nc > 0 ? L.st_off + round_up(st_bytes) : 0;
+    return L;
+}
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char *name, const void *p, size_t bytes) {
+    uintptr_t lo = (uintptr_t)p;
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_workspace_bytes(const ssd_shape *shape, int chunk_size, ssd_dtype dtype) {
+    if (check_shape(shape, chunk_size, dtype) != SSD_OK) return 0;
+    return layout_of(shape, chunk_size).total;
+}
+
+ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_dtype dtype,
+                                    ssd_workspace_layout *out) {
+    if (!out) return fail(SSD_ERR_NULL, "out is NULL");
+    ssd_status st = check_shape(shape, chunk_size, dtype);
+    if (st != SSD_OK) return st;
+    const Layout L = layout_of(shape, chunk_size);
+    out->cumsum_offset = L.cs_off;
+    out->states_offset = L.st_off;
+    out->total_bytes = L.total;
+    out->nchunks = L.nc;
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                              const float *D, const float *init_state, int chunk_size, void *y,
+                              float *final_state, const int32_t *state_out_idx, float *state_out,
+                              const ssd_shape *shape, ssd_dtype dtype, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+    ssd_status st = check_shape(shape, chunk_size, dtype);
+    if (st != SSD_OK) return st;
+    const int64_t b = shape->batch, T = shape->seqlen, H = shape->nheads, P = shape->headdim, N = shape->dstate,
+                  G = shape->ngroups;
+    if ((state_out == nullptr) != (state_out_idx == nullptr))
+        return fail(SSD_ERR_ARGS, "state_out and state_out_idx must be given together");
+
+    const size_t esz = dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const size_t n_tok = (size_t)b * T;
+    const size_t x_bytes = n_tok * H * P * esz, bc_bytes = n_tok * G * N * esz;
+    const size_t dt_bytes = n_tok * H * sizeof(float), state_bytes = (size_t)b * H * P * N * sizeof(float);
+    const Layout L = layout_of(shape, chunk_size);
+
+    if (n_tok > 0) {
+        if (!x || !dt || !A || !B || !C || !y) return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
+        if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+        if (workspace_bytes < L.total)
+            return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    }
+    if (b > 0 && state_out_idx == nullptr && state_out != nullptr) return fail(SSD_ERR_ARGS, "state_out_idx missing");
+
+    const void *aligned16[] = {x, B, C, y, init_state, final_state, state_out, workspace};
+    const char *names16[] = {"x", "B", "C", "y", "init_state", "final_state", "state_out", "workspace"};
+    for (int k = 0; k < 8; ++k)
+        if ((uintptr_t)aligned16[k] % 16 != 0) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", names16[k]);
+    const void *aligned4[] = {dt, A, D, state_out_idx};
+    const char *names4[] = {"dt", "A", "D", "state_out_idx"};
+    for (int k = 0; k < 4; ++k)
+        if ((uintptr_t)aligned4[k] % 4 != 0) return fail(SSD_ERR_ALIGN, "%s is not 4-byte aligned", names4[k]);
+
+    const Range outs[] = {range("y", y, x_bytes), range("final_state", final_state, state_bytes),
+                          range("state_out", state_out, state_bytes)};
+    const Range others[] = {range("x", x, x_bytes), range("dt", dt, dt_bytes), range("A", A, H * sizeof(float)),
+                            range("B", B, bc_bytes), range("C", C, bc_bytes), range("D", D, H * sizeof(float)),
+                            range("init_state", init_state, state_bytes),
+                            range("state_out_idx", state_out_idx, b * sizeof(int32_t)),
+                            range("workspace", workspace, L.total)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range &o : others)
+            if (overlaps(outs[i], o)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, o.name);
+        for (int k = i + 1; k < 3; ++k)
+            if (overlaps(outs[i], outs[k])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[k].name);
+    }
+
+    if (b == 0 || (T == 0 && !final_state && !state_out)) return SSD_OK;  // nothing to enqueue
+
+    ssd::Params p;
+    p.x = x;
+    p.dt = dt;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.init_state = init_state;
+    p.state_out_idx = state_out_idx;
+    p.y = y;
+    p.final_state = final_state;
+    p.state_out = state_out;
+    p.cs = workspace ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.cs_off) : nullptr;
+    p.states = workspace ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.st_off) : nullptr;
+    p.batch = b;
+    p.seqlen = T;
+    p.nheads = (int)H;
+    p.headdim = (int)P;
+    p.dstate = (int)N;
+    p.ngroups = (int)G;
+    p.chunk = chunk_size;
+    p.nchunks = (int)L.nc;
+    p.heads_per_group = (int)(H / G);
+    const ssd::Elem e = dtype == SSD_DTYPE_BF16 ? ssd::Elem::BF16 : ssd::Elem::F32;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+    (void)hipGetLastError();  // start from a clean error state
+    hipError_t err;
+    const char *step = "";
+    if (T == 0) {
+        step = "empty_sequence";
+        err = ssd::launch_empty_sequence(p, stream);
+    } else {
+        do {
+            step = "chunk_cumsum";
+            if ((err = ssd::launch_chunk_cumsum(p, stream)) != hipSuccess) break;
+            step = "chunk_state";
+            if ((err = ssd::launch_chunk_state(p, e, stream)) != hipSuccess) break;
+            step = "state_pass";
+            if ((err = ssd::launch_state_pass(p, stream)) != hipSuccess) break;
+            step = "chunk_output";
+            if ((err = ssd::launch_chunk_output(p, e, stream)) != hipSuccess) break;
+            if (state_out) {
+                step = "state_at_index";
+                if ((err = ssd::launch_state_at_index(p, e, stream)) != hipSuccess) break;
+            }
+        } while (false);
+    }
+    if (err != hipSuccess) return fail(SSD_ERR_HIP, "%s launch failed: %s", step, hipGetErrorString(err));
+    return SSD_OK;
+}
+
+const char *ssd_status_string(ssd_status s) {
+    switch (s) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid shape";
+        case SSD_ERR_CHUNK: return "unsupported chunk_size";
+        case SSD_ERR_ALIGN: return "misaligned pointer";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_ALIAS: return "an output overlaps another buffer";
+        case SSD_ERR_ARGS: return "inconsistent arguments";
+        case SSD_ERR_HIP: return "HIP launch failure";
+        case SSD_ERR_UNSUPPORTED: return "unsupported size";
+    }
+    return "unknown status";
+}
+
+const char *ssd_last_error(void) { return g_last_error.c_str(); }
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_06_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_CHUNK, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS, ERR_ARGS, ERR_HIP, ERR_UNSUPPORTED = range(10)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_built():
+    assert os.path.exists(ssd.library_path()), "run python -m mamba_ssd_scan_06_amd.build"
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ssd.library_path())
+    names = declared_functions()
+    assert {"ssd_chunk_scan_fwd", "ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_status_string",
+            "ssd_last_error", "ssd_abi_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in ssd.h but not exported"
+
+
+def test_abi_version():
+    assert ssd.ssd_abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(10):
+        assert ssd.ssd_status_string(code) not in ("", "unknown status")
+    assert ssd.ssd_status_string(99) == "unknown status"
+
+
+def shape(b=2, T=100, H=4, P=64, N=128, G=2):
+    return ssd.make_shape(b, T, H, P, N, G)
+
+
+def test_workspace_bytes_formula():
+    s = shape()
+    nc = (100 + 63) // 64
+    cs = 2 * 4 * nc * 64 * 4
+    st = 2 * nc * 4 * 64 * 128 * 4
+    rnd = lambda v: (v + 255) // 256 * 256
+    assert ssd.ssd_workspace_bytes(s, 64, ssd.SSD_DTYPE_BF16) == rnd(cs) + rnd(st)
+    lay = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_BF16)
+    assert lay.nchunks == nc and lay.cumsum_offset == 0 and lay.states_offset == rnd(cs)
+    assert ssd.ssd_workspace_bytes(shape(T=0), 64, ssd.SSD_DTYPE_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,chunk,code", [
+    (dict(H=4, G=3), 64, ERR_SHAPE),
+    (dict(b=-1), 64, ERR_SHAPE),
+    (dict(P=0), 64, ERR_SHAPE),
+    (dict(), 48, ERR_CHUNK),
+    (dict(), 512, ERR_CHUNK),
+    (dict(), 4, ERR_CHUNK),
+    (dict(P=48), 64, ERR_UNSUPPORTED),
+    (dict(P=256), 64, ERR_UNSUPPORTED),
+    (dict(N=8), 64, ERR_UNSUPPORTED),
+    (dict(N=512), 64, ERR_UNSUPPORTED),
+])
+def test_shape_errors(kw, chunk, code):
+    s = shape(**kw)
+    assert ssd.ssd_workspace_bytes(s, chunk, ssd.SSD_DTYPE_BF16) == 0
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_get_workspace_layout(s, chunk, ssd.SSD_DTYPE_BF16)
+    assert e.value.status == code
+    assert ssd.ssd_last_error() != ""
+
+
+def test_fp32_lds_budget():
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_get_workspace_layout(shape(P=128, N=256), 64, ssd.SSD_DTYPE_F32)
+    assert e.value.status == ERR_UNSUPPORTED
+    ssd.ssd_get_workspace_layout(shape(P=128, N=256), 64, ssd.SSD_DTYPE_BF16)
+
+
+# Fake, never-dereferenced device addresses: the checks below return before any launch.
+BASE = 1 << 40
+MB = 1 << 20
+
+
+class Args:
+    def __init__(self, s, chunk=64, dtype=ssd.SSD_DTYPE_BF16):
+        self.s, self.chunk, self.dtype = s, chunk, dtype
+        self.p = {k: BASE + i * 256 * MB for i, k in enumerate(
+            ["x", "dt", "A", "B", "C", "D", "init", "y", "final", "idx", "sout", "ws"])}
+        self.ws_bytes = ssd.ssd_workspace_bytes(s, chunk, dtype)
+        self.p["idx"] = None
+        self.p["sout"] = None
+
+    def call(self):
+        lib = ssd._load()
+        v = lambda k: None if self.p[k] is None else ctypes.c_void_p(self.p[k])
+        return lib.ssd_chunk_scan_fwd(v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("init"), self.chunk,
+                                      v("y"), v("final"), v("idx"), v("sout"), ctypes.byref(self.s), self.dtype,
+                                      v("ws"), self.ws_bytes, None)
+
+
+@pytest.mark.parametrize("key", ["x", "dt", "A", "B", "C", "y"])
+def test_null_required(key):
+    a = Args(shape())
+    a.p[key] = None
+    assert a.call() == ERR_NULL
+
+
+def test_workspace_errors():
+    a = Args(shape())
+    a.p["ws"] = None
+    assert a.call() == ERR_WORKSPACE
+    a = Args(shape())
+    a.ws_bytes -= 1
+    assert a.call() == ERR_WORKSPACE
+
+
+def test_state_out_requires_index():
+    a = Args(shape())
+    a.p["sout"] = BASE + 20 * 256 * MB
+    assert a.call() == ERR_ARGS
+    a = Args(shape())
+    a.p["idx"] = BASE + 20 * 256 * MB
+    assert a.call() == ERR_ARGS
+
+
+@pytest.mark.parametrize("key,off", [("x", 8), ("y", 2), ("B", 4), ("final", 8), ("ws", 4), ("dt", 2), ("A", 1)])
+def test_alignment(key, off):
+    a = Args(shape())
+    a.p[key] += off
+    assert a.call() == ERR_ALIGN
+
+
+@pytest.mark.parametrize("out,inp", [("y", "x"), ("final", "init"), ("y", "ws"), ("final", "y")])
+def test_alias(out, inp):
+    a = Args(shape())
+    a.p[out] = a.p[inp] + 1024
+    assert a.call() == ERR_ALIAS
+
+
+def test_empty_batch_is_noop():
+    a = Args(shape(b=0))
+    for k in a.p:
+        a.p[k] = None
+    assert a.call() == OK
+
+
+def test_empty_sequence_without_state_outputs_is_noop():
+    a = Args(shape(T=0))
+    a.p["final"] = None
+    a.ws_bytes = 0
+    a.p["ws"] = None
+    assert a.call() == OK

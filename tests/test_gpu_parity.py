@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.  Every case prints its name, shape and seed first."""
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_scan_06_amd as ssd
+import oracle
+import ssd_inputs
+from ssd_testing import TOL, device_inputs, gpu_run, oracle_run, relerr, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check(name, got, ref, tol):
+    e = relerr(got, ref)
+    print(f"  {name}: max rel err {e:.3e} (tol {tol:.0e})", flush=True)
+    assert e <= tol, f"{name}: {e:.3e} > {tol:.0e}"
+    return e
+
+
+@pytest.fixture(scope="module", autouse=True)
+def library_loaded():
+    # No fallback exists: the HIP library must be there on a GPU machine.
+    assert torch.cuda.is_available()
+    assert ssd.ssd_abi_version() == 1
+
+
+# ----------------------------------------------------------- full workloads
+@pytest.mark.parametrize("name", ssd_inputs.WORKLOAD_ORDER)
+def test_workload_full_size(name):
+    wl = ssd_inputs.WORKLOADS[name]
+    announce(f"{name} b={wl.batch} T={wl.seqlen} H={wl.nheads} P={wl.headdim} N={wl.dstate} "
+             f"G={wl.ngroups} Q={wl.chunk} {wl.dtype} seed={wl.seed}")
+    inp = ssd_inputs.generate(wl)
+    tol = TOL[wl.dtype]
+    ref = oracle_run(inp)
+    dev = device_inputs(inp)
+    got = gpu_run(inp, dev=dev)
+    check("y", got["y"], ref["y"], tol)
+    check("final_state", got["final"], ref["final"], tol)
+    if wl.state_out:
+        check("state_out", got["state_out"], ref["state_out"], tol)
+    # Without the D skip, so that D*x cannot hide an error in the scan itself.
+    got_nod = gpu_run(inp, dev=dev, use_D=False)
+    ref_nod = ref["y"] - inp.D[None, None, :, None].astype(np.float64) * inp.x.astype(np.float64)
+    check("y (D = None)", got_nod["y"], ref_nod, tol)
+
+
+# -------------------------------------------------- individual steps (a1-a6)
+STEP_CASES = [
+    workload("steps_bf16", 2, 700, 6, 64, 128, 2, 128, "bf16", init_state=True, seed=31),
+    workload("steps_f32", 2, 300, 4, 32, 64, 1, 64, "f32", init_state=True, seed=32),
+    workload("steps_n256", 1, 600, 4, 64, 256, 1, 256, "bf16", seed=33),
+]
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_step_chunk_cumsum(wl):
+    announce(f"chunk cumsum {wl}")
+    inp = ssd_inputs.generate(wl)
+    got = gpu_run(inp, return_workspace=True)
+    ref = oracle.chunk_cumsum(inp.dt, inp.A, wl.chunk)
+    err = np.max(np.abs(got["cs"] - ref) / np.maximum(np.abs(ref), 1.0))
+    print(f"  cs: max err {err:.3e}")
+    assert err <= 2e-6
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_step_chunk_states_and_passing(wl):
+    # After the call the workspace holds, for every chunk, the state entering
+    # it: the chunk states (green) passed through the scan over chunks (yellow).
+    announce(f"chunk states {wl}")
+    inp = ssd_inputs.generate(wl)
+    got = gpu_run(inp, return_workspace=True)
+    ref = oracle_run(inp, chunk=wl.chunk)
+    check("states entering each chunk", got["states"], ref["chunk_states"], TOL[wl.dtype])
+    check("final_state", got["final"], ref["final"], TOL[wl.dtype])
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_step_single_chunk_state(wl):
+    # One chunk, zero initial state: final_state is exactly that chunk's state.
+    w1 = workload(wl.name + "_one", wl.batch, wl.chunk - 3, wl.nheads, wl.headdim, wl.dstate, wl.ngroups,
+                  wl.chunk, wl.dtype, seed=wl.seed + 1)
+    announce(f"single chunk state {w1}")
+    inp = ssd_inputs.generate(w1)
+    check("chunk state", gpu_run(inp)["final"], oracle_run(inp)["final"], TOL[wl.dtype])
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_step_intra_chunk_only(wl):
+    # One chunk, zero initial state, no D: y is the diagonal block alone.
+    w1 = workload(wl.name + "_diag", wl.batch, wl.chunk, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk,
+                  wl.dtype, seed=wl.seed + 2)
+    announce(f"intra-chunk only {w1}")
+    inp = ssd_inputs.generate(w1)
+    check("y diagonal block", gpu_run(inp, use_D=False)["y"], oracle_run(inp, use_D=False)["y"], TOL[wl.dtype])
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_step_state_to_output_only(wl):
+    # x = 0 with an initial state: y is the state-to-output term alone.
+    w1 = workload(wl.name + "_blue", wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk,
+                  wl.dtype, init_state=True, seed=wl.seed + 3)
+    announce(f"state-to-output only {w1}")
+    inp = ssd_inputs.generate(w1)
+    inp.x = np.zeros_like(inp.x)
+    if inp.x_bits is not None:
+        inp.x_bits = np.zeros_like(inp.x_bits)
+    got, ref = gpu_run(inp), oracle_run(inp)
+    check("y from the initial state", got["y"], ref["y"], TOL[wl.dtype])
+    check("final_state (pure decay)", got["final"], ref["final"], TOL[wl.dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_state_at_index(dtype):
+    T, Q = 150, 32
+    wl = workload("at_index_" + dtype, 8, T, 4, 32, 32, 2, Q, dtype, init_state=True, state_out=True, seed=41)
+    announce(f"state at index {wl}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    for idx in ([-1, 0, 1, 31, 32, 33, 100, T - 1], [T - 1, 63, 64, 65, 5, 127, 128, 149]):
+        inp.state_out_idx = np.array(idx, np.int32)
+        dev["state_out_idx"] = torch.from_numpy(inp.state_out_idx).cuda()
+        got, ref = gpu_run(inp, dev=dev), oracle_run(inp)
+        check(f"state_out {idx}", got["state_out"], ref["state_out"], TOL[dtype])
+        check("final_state", got["final"], ref["final"], TOL[dtype])
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_size_invariance(dtype):
+    wl = workload("chunk_inv_" + dtype, 2, 300, 4, 64, 64, 2, 64, dtype, init_state=True, seed=51)
+    announce(f"chunk-size invariance {wl}")
+    inp = ssd_inputs.generate(wl)
+    ref = oracle_run(inp)
+    dev = device_inputs(inp)
+    ys = {}
+    for Q in (8, 16, 32, 64, 128, 256):
+        got = gpu_run(inp, chunk=Q, dev=dev)
+        check(f"Q={Q} y", got["y"], ref["y"], TOL[dtype])
+        check(f"Q={Q} final", got["final"], ref["final"], TOL[dtype])
+        ys[Q] = got["y"]
+    for Q in ys:
+        assert relerr(ys[Q], ys[64]) <= 2 * TOL[dtype]
+
+
+@pytest.mark.parametrize("m", [64, 100, 1])
+def test_two_halves(m):
+    wl = workload("halves", 2, 257, 4, 64, 128, 1, 64, "bf16", init_state=True, seed=61)
+    announce(f"two halves m={m} {wl}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    full = gpu_run(inp, dev=dev)
+    ref = oracle_run(inp)
+    first = {k: (v[:, :m].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in dev.items()}
+    second = {k: (v[:, m:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in dev.items()}
+    y1, f1, _ = ssd.ssd_chunk_scan_fwd(first["x"], first["dt"], first["A"], first["B"], first["C"], first["D"],
+                                       first["init_state"], 64)
+    y2, f2, _ = ssd.ssd_chunk_scan_fwd(second["x"], second["dt"], second["A"], second["B"], second["C"],
+                                       second["D"], f1, 64)
+    torch.cuda.synchronize()
+    y = torch.cat([y1, y2], dim=1).float().cpu().numpy()
+    check("halves y vs oracle", y, ref["y"], 2e-2)
+    check("halves final vs oracle", f2.cpu().numpy(), ref["final"], 2e-2)
+    check("halves y vs one call", y, full["y"], 2e-2)
+
+
+def test_determinism():
+    wl = ssd_inputs.WORKLOADS["llama3_8b_hybrid"]
+    wl = workload("determinism", 2, 1000, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk, "bf16",
+                  init_state=True, state_out=True, seed=71)
+    announce(f"determinism {wl}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    runs = [gpu_run(inp, dev=dev) for _ in range(3)]
+    for r in runs[1:]:
+        for k in ("y", "final", "state_out"):
+            assert np.array_equal(r[k], runs[0][k]), f"{k} differs between identical calls"
+
+
+def test_guard_canaries():
+    wl = workload("canaries", 2, 200, 4, 64, 128, 2, 64, "bf16", init_state=True, state_out=True, seed=81)
+    announce(f"canaries {wl}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    pad = 4096
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n]
+    ybuf, y = guarded(dev["x"].numel(), torch.bfloat16)
+    n_state = 2 * 4 * 64 * 128
+    fbuf, fin = guarded(n_state, torch.float32)
+    sbuf, sout = guarded(n_state, torch.float32)
+    ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], dev["init_state"], 64,
+                           dev["state_out_idx"], y=y.view(dev["x"].shape), final_state=fin.view(2, 4, 64, 128),
+                           state_out=sout.view(2, 4, 64, 128))
+    torch.cuda.synchronize()
+    for buf in (ybuf, fbuf, sbuf):
+        assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[-pad:].float()).all(), "write outside output"
+        assert torch.isfinite(buf[pad:-pad].float()).all(), "output not fully written"
+    ref = oracle_run(inp)
+    check("y", y.view(dev["x"].shape).float().cpu().numpy(), ref["y"], 2e-2)
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE = [
+    # b, T, H, P, N, G, Q, dtype
+    (1, 1, 1, 16, 16, 1, 8, "f32"),
+    (3, 7, 2, 16, 32, 2, 8, "bf16"),
+    (2, 33, 4, 32, 64, 4, 32, "bf16"),
+    (1, 257, 2, 64, 256, 1, 256, "bf16"),
+    (2, 255, 8, 128, 256, 2, 128, "bf16"),
+    (1, 129, 3, 128, 16, 3, 16, "bf16"),
+    (2, 100, 4, 64, 128, 1, 256, "f32"),
+    (1, 1000, 2, 16, 16, 2, 64, "f32"),
+    (4, 9, 32, 128, 128, 8, 8, "bf16"),
+    (1, 64, 1, 64, 64, 1, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "b{}_T{}_H{}_P{}_N{}_G{}_Q{}_{}".format(*c))
+def test_edge_shapes(case):
+    b, T, H, P, N, G, Q, dtype = case
+    wl = workload("edge", b, T, H, P, N, G, Q, dtype, init_state=True, state_out=True, seed=91 + T)
+    announce(f"edge {wl}")
+    inp = ssd_inputs.generate(wl)
+    got, ref = gpu_run(inp), oracle_run(inp)
+    for k in ("y", "final", "state_out"):
+        check(k, got[k], ref[k], TOL[dtype])
+
+
+def test_empty_sequence():
+    announce("empty sequence T=0")
+    h0 = torch.randn(2, 4, 64, 128, device="cuda")
+    x = torch.empty(2, 0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.empty(2, 0, 1, 128, dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty(2, 0, 4, device="cuda")
+    A = -torch.ones(4, device="cuda")
+    idx = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    y, fin, sout = ssd.ssd_chunk_scan_fwd(x, dt, A, B, B, None, h0, 64, idx)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(fin, h0) and torch.equal(sout, h0)
+    _, fin0, _ = ssd.ssd_chunk_scan_fwd(x, dt, A, B, B, None, None, 64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin0) == 0
+
+
+def test_empty_batch():
+    announce("empty batch b=0")
+    x = torch.empty(0, 16, 4, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.empty(0, 16, 1, 128, dtype=torch.bfloat16, device="cuda")
+    y, fin, _ = ssd.ssd_chunk_scan_fwd(x, torch.empty(0, 16, 4, device="cuda"), -torch.ones(4, device="cuda"),
+                                       B, B, None, None, 64)
+    assert y.numel() == 0 and fin.numel() == 0
