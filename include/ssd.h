@@ -145,6 +145,25 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const ssd_shape *shape, ssd_dtype dtype,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Same as ssd_chunk_scan_fwd, and additionally records caller-created HIP
+ * events (hipEvent_t passed as void*) on hip_stream around the kernels, so
+ * that a caller can time each kernel in place:
+ *   marks[0]  before the first kernel,
+ *   marks[k]  after the k-th kernel launched (k = 1 .. n_marks-1).
+ * On SSD_OK, *n_kernels (if non-NULL) is the number of kernels launched and
+ * kernel_names[k-1] (if kernel_names is non-NULL and k < n_marks) names the
+ * kernel that marks[k] ends.  Marks beyond the kernels launched are not
+ * recorded.  Used by the benchmark to measure per-kernel durations. */
+ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const float *init_state, int chunk_size,
+                                     void *y, float *final_state,
+                                     const int32_t *state_out_idx, float *state_out,
+                                     const ssd_shape *shape, ssd_dtype dtype,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream,
+                                     void *const *marks, int n_marks, int *n_kernels,
+                                     const char **kernel_names);
+
 /* Static description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

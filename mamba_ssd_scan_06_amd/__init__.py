@@ -15,7 +15,8 @@ import os
 
 __all__ = [
     "SsdError", "ssd_abi_version", "ssd_status_string", "ssd_last_error", "ssd_workspace_bytes",
-    "ssd_get_workspace_layout", "ssd_chunk_scan_fwd", "workspace_views", "library_path",
+    "ssd_get_workspace_layout", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_marked", "workspace_views",
+    "library_path",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,10 @@ def _load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m mamba_ssd_scan_06_amd.build`")
+    # torch ships its own HIP runtime under the same soname; loading torch
+    # first makes libssd bind to that one, so torch's streams and memory are
+    # the library's too (one runtime per process).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     shp = ctypes.POINTER(ssd_shape)
@@ -65,6 +70,10 @@ def _load():
     lib.ssd_get_workspace_layout.restype = i32
     lib.ssd_chunk_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp, sz, vp]
     lib.ssd_chunk_scan_fwd.restype = i32
+    lib.ssd_chunk_scan_fwd_marked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp, sz, vp,
+                                              ctypes.POINTER(vp), i32, ctypes.POINTER(i32),
+                                              ctypes.POINTER(ctypes.c_char_p)]
+    lib.ssd_chunk_scan_fwd_marked.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -129,6 +138,23 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, init_state=None, chunk_size: int 
     (y, final_state or None, state_out or None).  Raises SsdError on any
     status other than SSD_OK.
     """
+    y, final_state, state_out, _ = _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state,
+                                        return_final_state, state_out, workspace, stream, None)
+    return y, final_state, state_out
+
+
+def ssd_chunk_scan_fwd_marked(x, dt, A, B, C, D=None, init_state=None, chunk_size: int = 256,
+                              state_out_idx=None, *, marks, y=None, final_state=None,
+                              return_final_state: bool = True, state_out=None, workspace=None, stream=None):
+    """ssd_chunk_scan_fwd that also records the HIP events `marks` (raw
+    hipEvent_t handles as ints): marks[0] before the first kernel, marks[k]
+    after the k-th.  Returns (y, final_state, state_out, kernel_names)."""
+    return _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state, return_final_state,
+                state_out, workspace, stream, marks)
+
+
+def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state, return_final_state, state_out,
+         workspace, stream, marks):
     import torch
 
     lib = _load()
@@ -164,12 +190,19 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, init_state=None, chunk_size: int 
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else None
-    status = lib.ssd_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
-                                    int(chunk_size), _ptr(y), _ptr(final_state), _ptr(state_out_idx),
-                                    _ptr(state_out), ctypes.byref(shape), code, _ptr(workspace),
-                                    int(workspace.numel()), ctypes.c_void_p(stream) if stream else None)
-    _check(status)
-    return y, final_state, state_out
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), int(chunk_size), _ptr(y),
+            _ptr(final_state), _ptr(state_out_idx), _ptr(state_out), ctypes.byref(shape), code, _ptr(workspace),
+            int(workspace.numel()), ctypes.c_void_p(stream) if stream else None)
+    if marks is None:
+        _check(lib.ssd_chunk_scan_fwd(*args))
+        return y, final_state, state_out, None
+    n = len(marks)
+    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(m)) for m in marks])
+    names = (ctypes.c_char_p * max(n, 1))()
+    count = ctypes.c_int(0)
+    _check(lib.ssd_chunk_scan_fwd_marked(*args, arr, n, ctypes.byref(count), names))
+    used = min(count.value, n - 1) if n > 0 else 0
+    return y, final_state, state_out, [names[k].decode() for k in range(used)]
 
 
 def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):

@@ -96,6 +96,34 @@ bool overlaps(const Range &a, const Range &b) {
     return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
 }
 
+// Runs the launch sequence, stops at the first failure and records the
+// caller's timing marks after each kernel.
+struct Launcher {
+    hipStream_t stream;
+    void *const *marks;
+    int n_marks;
+    const char **names;
+    hipError_t err = hipSuccess;
+    const char *failed_step = "";
+    int count = 0;
+
+    template <typename F>
+    void step(const char *name, F &&launch) {
+        if (err != hipSuccess) return;
+        err = launch();
+        if (err != hipSuccess) {
+            failed_step = name;
+            return;
+        }
+        ++count;
+        if (count < n_marks) {
+            err = hipEventRecord(static_cast<hipEvent_t>(marks[count]), stream);
+            if (err != hipSuccess) failed_step = "event record";
+            if (names) names[count - 1] = name;
+        }
+    }
+};
+
 }  // namespace
 
 extern "C" {
@@ -118,11 +146,13 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     return SSD_OK;
 }
 
-ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B, const void *C,
-                              const float *D, const float *init_state, int chunk_size, void *y,
-                              float *final_state, const int32_t *state_out_idx, float *state_out,
-                              const ssd_shape *shape, ssd_dtype dtype, void *workspace, size_t workspace_bytes,
-                              void *hip_stream) {
+ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float *A, const void *B,
+                                     const void *C, const float *D, const float *init_state, int chunk_size,
+                                     void *y, float *final_state, const int32_t *state_out_idx,
+                                     float *state_out, const ssd_shape *shape, ssd_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, void *hip_stream, void *const *marks, int n_marks,
+                                     int *n_kernels, const char **kernel_names) {
+    if (n_marks < 0 || (n_marks > 0 && !marks)) return fail(SSD_ERR_ARGS, "marks must hold n_marks events");
     ssd_status st = check_shape(shape, chunk_size, dtype);
     if (st != SSD_OK) return st;
     const int64_t b = shape->batch, T = shape->seqlen, H = shape->nheads, P = shape->headdim, N = shape->dstate,
@@ -196,29 +226,31 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
     (void)hipGetLastError();  // start from a clean error state
-    hipError_t err;
-    const char *step = "";
+    Launcher run{stream, marks, n_marks, kernel_names};
+    if (n_marks > 0) run.err = hipEventRecord(static_cast<hipEvent_t>(marks[0]), stream);
     if (T == 0) {
-        step = "empty_sequence";
-        err = ssd::launch_empty_sequence(p, stream);
+        run.step("empty_sequence", [&] { return ssd::launch_empty_sequence(p, stream); });
     } else {
-        do {
-            step = "chunk_cumsum";
-            if ((err = ssd::launch_chunk_cumsum(p, stream)) != hipSuccess) break;
-            step = "chunk_state";
-            if ((err = ssd::launch_chunk_state(p, e, stream)) != hipSuccess) break;
-            step = "state_pass";
-            if ((err = ssd::launch_state_pass(p, stream)) != hipSuccess) break;
-            step = "chunk_output";
-            if ((err = ssd::launch_chunk_output(p, e, stream)) != hipSuccess) break;
-            if (state_out) {
-                step = "state_at_index";
-                if ((err = ssd::launch_state_at_index(p, e, stream)) != hipSuccess) break;
-            }
-        } while (false);
+        run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
+        run.step("chunk_state", [&] { return ssd::launch_chunk_state(p, e, stream); });
+        run.step("state_pass", [&] { return ssd::launch_state_pass(p, stream); });
+        run.step("chunk_output", [&] { return ssd::launch_chunk_output(p, e, stream); });
+        if (state_out) run.step("state_at_index", [&] { return ssd::launch_state_at_index(p, e, stream); });
     }
-    if (err != hipSuccess) return fail(SSD_ERR_HIP, "%s launch failed: %s", step, hipGetErrorString(err));
+    if (run.err != hipSuccess)
+        return fail(SSD_ERR_HIP, "%s launch failed: %s", run.failed_step, hipGetErrorString(run.err));
+    if (n_kernels) *n_kernels = run.count;
     return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                              const float *D, const float *init_state, int chunk_size, void *y,
+                              float *final_state, const int32_t *state_out_idx, float *state_out,
+                              const ssd_shape *shape, ssd_dtype dtype, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+    return ssd_chunk_scan_fwd_marked(x, dt, A, B, C, D, init_state, chunk_size, y, final_state, state_out_idx,
+                                     state_out, shape, dtype, workspace, workspace_bytes, hip_stream, nullptr, 0,
+                                     nullptr, nullptr);
 }
 
 const char *ssd_status_string(ssd_status s) {
