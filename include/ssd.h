@@ -91,15 +91,23 @@ typedef struct {
 /* Where the intermediates live inside the workspace after a call (byte
  * offsets from the workspace pointer).  Exposed so that the individual steps
  * can be checked:
- *   cumsum  fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
- *           cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
- *           past seqlen count as dt = 0.
- *   states  fp32 [batch, nchunks, nheads, headdim, dstate]: after a call,
- *           entry c is the state entering chunk c (the initial state for
- *           c = 0).                                                        */
+ *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
+ *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
+ *            past seqlen count as dt = 0.
+ *   dt       fp32, same layout: dt per chunk (0 past seqlen).
+ *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
+ *            (within seqlen) of the 32-token block holding i.
+ *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: after a call,
+ *            entry c is the state entering chunk c (the initial state for
+ *            c = 0).
+ *   states16 bf16, same layout as states, rounded to nearest even (bf16
+ *            inputs only; offset 0 and no bytes for fp32 inputs).          */
 typedef struct {
     size_t cumsum_offset;
+    size_t dt_offset;
+    size_t dt_decay_offset;
     size_t states_offset;
+    size_t states16_offset;
     size_t total_bytes;
     int64_t nchunks;
 } ssd_workspace_layout;

@@ -36,8 +36,10 @@ class ssd_shape(ctypes.Structure):
 
 
 class ssd_workspace_layout(ctypes.Structure):
-    _fields_ = [("cumsum_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
-                ("total_bytes", ctypes.c_size_t), ("nchunks", ctypes.c_int64)]
+    _fields_ = [("cumsum_offset", ctypes.c_size_t), ("dt_offset", ctypes.c_size_t),
+                ("dt_decay_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
+                ("states16_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("nchunks", ctypes.c_int64)]
 
 
 class SsdError(RuntimeError):

@@ -21,6 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <type_traits>
+
 namespace ssd {
 
 using bf16 = __bf16;
@@ -107,6 +110,79 @@ __device__ __forceinline__ void load8_from_f32(Frag<bf16> &f, const float *p) {
 __device__ __forceinline__ void load8_from_f32(Frag<float> &f, const float *p) {
     f.lo = *reinterpret_cast<const f32x4 *>(p);
     f.hi = *reinterpret_cast<const f32x4 *>(p + 4);
+}
+
+// Fragment of an operand held in LDS with the contraction index k as the
+// row and the fragment's own index m contiguous ("[k][m]", row stride ld
+// elements).  Lane (m = col0 + lane%16, group g = lane/16) receives slots
+// 0..3 = rows k0+4g .. k0+4g+3 and slots 4..7 = rows k1+4g .. k1+4g+3 of
+// column m.
+// bf16 uses gfx950's ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element i%4 of the 8-byte loads of lanes 4k + i/4 (k = 0..3), so
+// source lane s points at row (k + s/4), columns col0 + 4*(s%4) .. +3, and
+// lane i ends up with column col0 + i of those four rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 ds_read_tr16(const bf16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(const_cast<bf16 *>(p)));
+}
+__device__ __forceinline__ void load_tr(Frag<bf16> &f, const bf16 *base, int ld, int k0, int k1, int col0) {
+    const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+    const int off = (4 * g + (s >> 2)) * ld + col0 + 4 * (s & 3);
+    const i16x4 a = ds_read_tr16(base + k0 * ld + off);
+    const i16x4 b = ds_read_tr16(base + k1 * ld + off);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    f.v = __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ void load_tr(Frag<float> &f, const float *base, int ld, int k0, int k1, int col0) {
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f.lo[r] = base[(k0 + 4 * g + r) * ld + col0 + i];
+        f.hi[r] = base[(k1 + 4 * g + r) * ld + col0 + i];
+    }
+}
+
+// Direct global -> LDS copies (gfx950 global_load_lds_dwordx4): every lane
+// of a wave copies 16 bytes from its own global address to
+// lds_wave_base + 16 * lane; lds_wave_base must be the same for the whole
+// wave.  Completion is tracked by vmcnt like any load; the kernels wait with
+// explicit s_waitcnt immediates and synchronise with a bare s_barrier, since
+// __syncthreads() would also wait for every copy still in flight.
+__device__ __forceinline__ void copy16_to_lds(const void *gsrc, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+// The wait is the s_waitcnt builtin (gfx9 immediate: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8), which the compiler's own wait insertion
+// takes into account; the barriers are asm with a memory clobber so that no
+// memory access is moved across them.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// Barrier after this wave's LDS stores have completed (its other loads may
+// still be in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// XOR swizzles of unpadded LDS tiles whose rows are W 16-byte pieces; the
+// copying lane of LDS piece `pos` of row r fetches global piece pos ^ swz(r).
+// Swizzle of a row of W 16-byte pieces read 16 bytes per lane down 16 rows.
+template <int W>
+__device__ __forceinline__ int swz_rows16(int r) {
+    if constexpr (W >= 16) return r & 15;
+    else return (r / (16 / W)) & (W - 1);
+}
+// Swizzle of a row of W pieces read through the transposing read (per 16 lanes:
+// 4 rows, 2 adjacent pieces).
+template <int W>
+__device__ __forceinline__ int swz_tr(int r) {
+    if constexpr (W >= 16) return 2 * (r & 7);
+    else if constexpr (W == 8) return 2 * ((r >> 1) & 3);
+    else if constexpr (W == 4) return 2 * ((r >> 2) & 1);
+    else return 0;
 }
 
 // Vector of 8 / 4 elements of T for global <-> register moves.

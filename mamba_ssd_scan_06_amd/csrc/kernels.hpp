@@ -22,8 +22,11 @@ struct Params {
     void *y;                  // [b,T,H,P]  T_elem
     float *final_state;       // [b,H,P,N] or null
     float *state_out;         // [b,H,P,N] or null
-    float *cs;                // workspace [b,H,nc,Q]
-    float *states;            // workspace [b,nc,H,P,N]
+    float *cs;                // workspace [b,H,nc,Q]: chunk-local cumulative log-decay
+    float *dtc;               // workspace [b,H,nc,Q]: dt per chunk (0 past the end)
+    float *dte;               // workspace [b,H,nc,Q]: dt_i * exp(cs_e - cs_i), e = last token of i's 32-token block
+    float *states;            // workspace [b,nc,H,P,N]: chunk states, then the state entering each chunk
+    void *states16;           // workspace [b,nc,H,P,N] bf16 copy of the state entering each chunk, or null
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
@@ -36,6 +39,9 @@ hipError_t launch_chunk_cumsum(const Params &p, hipStream_t stream);
 hipError_t launch_chunk_state(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_state_pass(const Params &p, hipStream_t stream);
 hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
+// Head-batched bf16 chunk outputs; returns hipErrorNotSupported when the
+// shape does not fit its LDS budget (the caller then uses launch_chunk_output).
+hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_at_index(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_empty_sequence(const Params &p, hipStream_t stream);
 

@@ -15,7 +15,7 @@
 
 #include <string>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "kernels.hpp"
 
 namespace {
@@ -67,18 +67,22 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, st_off, total;
+    size_t cs_off, dtc_off, dte_off, st_off, st16_off, total;
     int64_t nc;
 };
 
-Layout layout_of(const ssd_shape *s, int chunk) {
+Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     Layout L;
     L.nc = (s->seqlen + chunk - 1) / chunk;
-    const size_t cs_bytes = (size_t)s->batch * s->nheads * L.nc * chunk * sizeof(float);
-    const size_t st_bytes = (size_t)s->batch * L.nc * s->nheads * s->headdim * s->dstate * sizeof(float);
+    const size_t tab_bytes = round_up((size_t)s->batch * s->nheads * L.nc * chunk * sizeof(float));
+    const size_t n_st = (size_t)s->batch * L.nc * s->nheads * s->headdim * s->dstate;
     L.cs_off = 0;
-    L.st_off = round_up(cs_bytes);
-    L.total = L.nc > 0 ? L.st_off + round_up(st_bytes) : 0;
+    L.dtc_off = tab_bytes;
+    L.dte_off = 2 * tab_bytes;
+    L.st_off = 3 * tab_bytes;
+    L.st16_off = dtype == SSD_DTYPE_BF16 ? L.st_off + round_up(n_st * sizeof(float)) : 0;
+    const size_t end = dtype == SSD_DTYPE_BF16 ? L.st16_off + round_up(n_st * 2) : L.st_off + round_up(n_st * 4);
+    L.total = L.nc > 0 ? end : 0;
     return L;
 }
 
@@ -130,7 +134,7 @@ extern "C" {
 
 size_t ssd_workspace_bytes(const ssd_shape *shape, int chunk_size, ssd_dtype dtype) {
     if (check_shape(shape, chunk_size, dtype) != SSD_OK) return 0;
-    return layout_of(shape, chunk_size).total;
+    return layout_of(shape, chunk_size, dtype).total;
 }
 
 ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_dtype dtype,
@@ -138,9 +142,12 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     if (!out) return fail(SSD_ERR_NULL, "out is NULL");
     ssd_status st = check_shape(shape, chunk_size, dtype);
     if (st != SSD_OK) return st;
-    const Layout L = layout_of(shape, chunk_size);
+    const Layout L = layout_of(shape, chunk_size, dtype);
     out->cumsum_offset = L.cs_off;
+    out->dt_offset = L.dtc_off;
+    out->dt_decay_offset = L.dte_off;
     out->states_offset = L.st_off;
+    out->states16_offset = L.st16_off;
     out->total_bytes = L.total;
     out->nchunks = L.nc;
     return SSD_OK;
@@ -164,7 +171,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     const size_t n_tok = (size_t)b * T;
     const size_t x_bytes = n_tok * H * P * esz, bc_bytes = n_tok * G * N * esz;
     const size_t dt_bytes = n_tok * H * sizeof(float), state_bytes = (size_t)b * H * P * N * sizeof(float);
-    const Layout L = layout_of(shape, chunk_size);
+    const Layout L = layout_of(shape, chunk_size, dtype);
 
     if (n_tok > 0) {
         if (!x || !dt || !A || !B || !C || !y) return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
@@ -211,8 +218,12 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.y = y;
     p.final_state = final_state;
     p.state_out = state_out;
-    p.cs = workspace ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.cs_off) : nullptr;
-    p.states = workspace ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.st_off) : nullptr;
+    char *ws = static_cast<char *>(workspace);
+    p.cs = ws ? reinterpret_cast<float *>(ws + L.cs_off) : nullptr;
+    p.dtc = ws ? reinterpret_cast<float *>(ws + L.dtc_off) : nullptr;
+    p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
+    p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
+    p.states16 = ws && dtype == SSD_DTYPE_BF16 ? static_cast<void *>(ws + L.st16_off) : nullptr;
     p.batch = b;
     p.seqlen = T;
     p.nheads = (int)H;
@@ -234,7 +245,13 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
         run.step("chunk_state", [&] { return ssd::launch_chunk_state(p, e, stream); });
         run.step("state_pass", [&] { return ssd::launch_state_pass(p, stream); });
-        run.step("chunk_output", [&] { return ssd::launch_chunk_output(p, e, stream); });
+        run.step("chunk_output", [&] {
+            if (e == ssd::Elem::BF16) {
+                const hipError_t r = ssd::launch_chunk_output_heads(p, stream);
+                if (r != hipErrorNotSupported) return r;
+            }
+            return ssd::launch_chunk_output(p, e, stream);
+        });
         if (state_out) run.step("state_at_index", [&] { return ssd::launch_state_at_index(p, e, stream); });
     }
     if (run.err != hipSuccess)

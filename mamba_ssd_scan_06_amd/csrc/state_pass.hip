@@ -8,7 +8,9 @@
 // and a_c = exp(cs[c][Q-1]) its decay:
 //     h_{-1} = init_state (or 0),   h_c = a_c * h_{c-1} + S_c.
 // The kernel overwrites S_c with h_{c-1} (the state entering chunk c) and
-// writes h_{nc-1} to final_state.
+// writes h_{nc-1} to final_state.  For bf16 inputs it also stores h_{c-1}
+// rounded to bf16 (to nearest even), the form in which the output kernel
+// feeds it to the matrix cores.
 //
 // One lane per four consecutive state elements (b, h, p, n..n+3): 16-byte
 // coalesced loads and stores, sequential over chunks.  The chunk states of a
@@ -51,7 +53,10 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             if (c0 + k < nc) {
-                st[((b * nc + c0 + k) * H + h) * pn4 + q] = hc;
+                const int64_t at = ((b * nc + c0 + k) * H + h) * pn4 + q;
+                st[at] = hc;
+                if (p.states16)
+                    reinterpret_cast<bf16x4 *>(p.states16)[at] = bf16x4{(bf16)hc[0], (bf16)hc[1], (bf16)hc[2], (bf16)hc[3]};
                 hc = a[k] * hc + s[k];
             }
         }
