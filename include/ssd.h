@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -97,17 +97,20 @@ typedef struct {
  *   dt       fp32, same layout: dt per chunk (0 past seqlen).
  *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
  *            (within seqlen) of the 32-token block holding i.
- *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: after a call,
- *            entry c is the state entering chunk c (the initial state for
- *            c = 0).
- *   states16 bf16, same layout as states, rounded to nearest even (bf16
- *            inputs only; offset 0 and no bytes for fp32 inputs).          */
+ *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: entry c is the
+ *            state chunk c reaches from a zero initial state.
+ *   prev     dtype, same layout: entry c is the state entering chunk c,
+ *            rounded to nearest even to dtype; entry 0 is written only when
+ *            init_state is given (otherwise it is zero and left unwritten).
+ *   hj       fp32 [batch, nheads, headdim, dstate]: the state entering the
+ *            chunk that holds state_out_idx[b] (written only with state_out). */
 typedef struct {
     size_t cumsum_offset;
     size_t dt_offset;
     size_t dt_decay_offset;
     size_t states_offset;
-    size_t states16_offset;
+    size_t prev_offset;
+    size_t hj_offset;
     size_t total_bytes;
     int64_t nchunks;
 } ssd_workspace_layout;

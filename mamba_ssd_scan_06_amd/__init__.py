@@ -38,7 +38,8 @@ class ssd_shape(ctypes.Structure):
 class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("cumsum_offset", ctypes.c_size_t), ("dt_offset", ctypes.c_size_t),
                 ("dt_decay_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
-                ("states16_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("prev_offset", ctypes.c_size_t), ("hj_offset", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t),
                 ("nchunks", ctypes.c_int64)]
 
 
@@ -208,7 +209,9 @@ def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_stat
 
 
 def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
-    """(cs [b,H,nc,Q], states [b,nc,H,P,N]) fp32 views into a workspace after a call."""
+    """Views into a workspace after a call: cs [b,H,nc,Q] fp32, the chunk
+    states from a zero start [b,nc,H,P,N] fp32, and the states entering each
+    chunk [b,nc,H,P,N] in the input dtype (entry 0 only with init_state)."""
     import torch
 
     lay = ssd_get_workspace_layout(shape, chunk_size, dtype)
@@ -216,6 +219,8 @@ def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
     b, H, P, N = shape.batch, shape.nheads, shape.headdim, shape.dstate
     n_cs = b * H * nc * chunk_size
     n_st = b * nc * H * P * N
+    tdt, esz = (torch.bfloat16, 2) if dtype == SSD_DTYPE_BF16 else (torch.float32, 4)
     cs = workspace[lay.cumsum_offset:lay.cumsum_offset + 4 * n_cs].view(torch.float32).view(b, H, nc, chunk_size)
     st = workspace[lay.states_offset:lay.states_offset + 4 * n_st].view(torch.float32).view(b, nc, H, P, N)
-    return cs, st
+    prev = workspace[lay.prev_offset:lay.prev_offset + esz * n_st].view(tdt).view(b, nc, H, P, N)
+    return cs, st, prev

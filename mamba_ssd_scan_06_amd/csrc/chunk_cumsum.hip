@@ -16,68 +16,113 @@
 //   dte[i] = dt_i * exp(cs_e - cs_i), e = the last token (within the
 //            sequence) of i's 32-token block; e >= i, so the factor is <= 1.
 //
-// One workgroup per (b, c, 16 heads): the chunk's dt values for 16 heads are
-// staged in LDS (64-byte rows per token), each thread scans one segment of
-// Q/16 tokens of one head in fp64, segment offsets are added, and every entry
-// is rounded once to fp32 and stored as contiguous rows.
+// One wave per (b, c, h), four heads per workgroup.  The chunk's dt values of
+// the four heads are read with the token-major rows' contiguous 16 bytes per
+// token and transposed through LDS; each lane then owns Q/64 (at least one)
+// consecutive tokens, the prefix sum runs in fp64 (within the lane, then a
+// wave-wide scan of the lane totals), every entry is rounded once to fp32,
+// and each lane stores its tokens of a table row with one vector store.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ssd {
 namespace {
 
-constexpr int kHeads = 16;  // heads per workgroup
+constexpr int kHeads = 4;   // heads (waves) per workgroup
 constexpr int kBlock = 32;  // token block of dte
 
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(Params p) {
-    __shared__ double sum[256][kHeads + 1];    // [token][head]: dt, then prefix sums
-    __shared__ float dts[256][kHeads + 1];
-    __shared__ double seg_total[kHeads][kHeads + 1];
+__device__ inline double shfl_up_f64(double v, int delta, int lane) {
+    const int src = lane >= delta ? lane - delta : lane;
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2loint(v));
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+__device__ inline double shfl_f64(double v, int src) {
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2loint(v));
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+template <int V> struct FVec { typedef float __attribute__((ext_vector_type(V))) type; };
+template <> struct FVec<1> { typedef float type; };
+
+template <int VPT>
+__global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
+    __shared__ float dts[kHeads][256];
     const int c = blockIdx.x, h0 = blockIdx.y * kHeads;
     const int64_t b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int Q = p.chunk, H = p.nheads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Q = p.chunk, H = p.nheads, nc = p.nchunks;
     const int64_t L = p.seqlen;
     const int64_t t0 = (int64_t)c * Q;
     const int Qc = (int)(L - t0 < Q ? L - t0 : Q);
 
-    for (int e = tid; e < Q * kHeads; e += 256) {
-        const int i = e / kHeads, hl = e - i * kHeads;
-        const float v = (i < Qc && h0 + hl < H) ? p.dt[(b * L + t0 + i) * H + h0 + hl] : 0.f;
-        dts[i][hl] = v;
-        sum[i][hl] = (double)v;
+    // dt[b, t0 + i, h0 + k] -> dts[k][i]; consecutive threads read the four
+    // heads of one token, then the next token.
+    for (int e = tid; e < Q * kHeads; e += 64 * kHeads) {
+        const int i = e / kHeads, k = e - i * kHeads;
+        dts[k][i] = (i < Qc && h0 + k < H) ? p.dt[(b * L + t0 + i) * H + h0 + k] : 0.f;
     }
     __syncthreads();
+    const int h = h0 + wave;
+    if (h >= H) return;
 
-    const int nseg = Q < kHeads ? Q : kHeads;
-    const int seg_len = Q / nseg;
-    const int hl = tid % kHeads, s = tid / kHeads;
-    if (s < nseg) {
-        double run = 0.0;
-        for (int k = 0; k < seg_len; ++k) {
-            run += sum[s * seg_len + k][hl];
-            sum[s * seg_len + k][hl] = run;
+    // Tokens i = VPT*lane + v (lanes past the chunk hold zeros and store nothing).
+    const int i0 = VPT * lane;
+    float dtv[VPT];
+    double s[VPT];
+    double run = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        dtv[v] = i0 + v < Q ? dts[wave][i0 + v] : 0.f;
+        run += (double)dtv[v];
+        s[v] = run;
+    }
+    // Inclusive scan of the lane totals across the wave (Hillis-Steele).
+    double tot = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double o = shfl_up_f64(tot, d, lane);
+        if (lane >= d) tot += o;
+    }
+    const double before = tot - run;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) s[v] += before;
+
+    // Sum at e = end of the lane's 32-token block, clipped to the chunk's
+    // last valid token.  A lane's VPT tokens lie in one block.
+    const int ie = min(kBlock * (i0 / kBlock) + kBlock - 1, max(Qc - 1, 0));
+    double se = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const double o = shfl_f64(s[v], ie / VPT);
+        if (ie % VPT == v) se = o;
+    }
+
+    const double a = (double)p.A[h];
+    typename FVec<VPT>::type csv, dtcv, dtev;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const float cs_i = (float)(a * s[v]);
+        const float de = i0 + v < Qc ? dtv[v] * exp_neg((float)(a * (se - s[v]))) : 0.f;
+        if constexpr (VPT == 1) {
+            csv = cs_i;
+            dtcv = dtv[v];
+            dtev = de;
+        } else {
+            csv[v] = cs_i;
+            dtcv[v] = dtv[v];
+            dtev[v] = de;
         }
-        seg_total[s][hl] = run;
     }
-    __syncthreads();
-    if (s < nseg) {
-        double offset = 0.0;
-        for (int k = 0; k < s; ++k) offset += seg_total[k][hl];
-        for (int k = 0; k < seg_len; ++k) sum[s * seg_len + k][hl] += offset;
-    }
-    __syncthreads();
-    if (s >= nseg || h0 + hl >= H) return;
-
-    const double a = (double)p.A[h0 + hl];
-    const int64_t row = ((b * H + h0 + hl) * p.nchunks + c) * (int64_t)Q;
-    for (int k = 0; k < seg_len; ++k) {
-        const int i = s * seg_len + k;
-        const int e = min(kBlock * (i / kBlock) + kBlock - 1, max(Qc - 1, 0));
-        const float dti = dts[i][hl];
-        p.cs[row + i] = (float)(a * sum[i][hl]);
-        p.dtc[row + i] = dti;
-        p.dte[row + i] = i < Qc ? dti * exp_neg((float)(a * (sum[e][hl] - sum[i][hl]))) : 0.f;
+    if (i0 < Q) {
+        typedef typename FVec<VPT>::type FV;
+        const int64_t row = ((b * H + h) * nc + c) * (int64_t)Q + i0;
+        *reinterpret_cast<FV *>(p.cs + row) = csv;
+        *reinterpret_cast<FV *>(p.dtc + row) = dtcv;
+        *reinterpret_cast<FV *>(p.dte + row) = dtev;
     }
 }
 
@@ -85,7 +130,13 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(Params p) {
 
 hipError_t launch_chunk_cumsum(const Params &p, hipStream_t stream) {
     dim3 grid(p.nchunks, (p.nheads + kHeads - 1) / kHeads, (unsigned)p.batch);
-    hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(256), 0, stream, p);
+    if (p.chunk > 256) return hipErrorNotSupported;
+    if (p.chunk == 256)
+        hipLaunchKernelGGL(chunk_cumsum_kernel<4>, grid, dim3(64 * kHeads), 0, stream, p);
+    else if (p.chunk == 128)
+        hipLaunchKernelGGL(chunk_cumsum_kernel<2>, grid, dim3(64 * kHeads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(chunk_cumsum_kernel<1>, grid, dim3(64 * kHeads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -107,18 +107,12 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(Params p, int isplit)
     }
     const bool has_prev = c > 0 || p.init_state != nullptr;
     if (has_prev) {
-        const float *hp = p.states + ((b * nc + c) * H + h) * (int64_t)P * N;
+        const T *hp = reinterpret_cast<const T *>(p.prev) + ((b * nc + c) * H + h) * (int64_t)P * N;
         for (int q = tid; q < P * (NP / 8); q += 256) {
             const int pp = q / (NP / 8), n0 = 8 * (q - pp * (NP / 8));
             V8 v;
             if (n0 < N) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(hp + (int64_t)pp * N + n0);
-                const f32x4 bq = *reinterpret_cast<const f32x4 *>(hp + (int64_t)pp * N + n0 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = from_f32<T>(a[e]);
-                    v[e + 4] = from_f32<T>(bq[e]);
-                }
+                v = *reinterpret_cast<const V8 *>(hp + (int64_t)pp * N + n0);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(0.f);
@@ -403,18 +397,12 @@ __global__ __launch_bounds__(256) void chunk_output_dma_kernel(Params p, int isp
     }
     const bool has_prev = c > 0 || p.init_state != nullptr;
     if (has_prev) {
-        const float *hp = p.states + ((b * nc + c) * H + h) * (int64_t)P * N;
+        const T *hp = reinterpret_cast<const T *>(p.prev) + ((b * nc + c) * H + h) * (int64_t)P * N;
         for (int q = tid; q < P * (NP / 8); q += 256) {
             const int pp = q / (NP / 8), n0 = 8 * (q - pp * (NP / 8));
             V8 v;
             if (n0 < N) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(hp + (int64_t)pp * N + n0);
-                const f32x4 bq = *reinterpret_cast<const f32x4 *>(hp + (int64_t)pp * N + n0 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = (T)a[e];
-                    v[e + 4] = (T)bq[e];
-                }
+                v = *reinterpret_cast<const V8 *>(hp + (int64_t)pp * N + n0);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = (T)0.f;

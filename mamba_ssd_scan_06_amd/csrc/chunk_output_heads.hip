@@ -80,7 +80,6 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
     typedef typename Vec4<T>::type V4;
 
     __shared__ __align__(16) T xs[Cf::XE + Cf::X1E];  // head buffers 0 and 1; the B ring in buffer 1 during phase A
-    T *const xs0 = xs;
     T *const xs1 = xs + Cf::XE;
     __shared__ __align__(16) T hs[2][Cf::HE];
     __shared__ __align__(16) float tab[2][3][256];  // cs, dt, dt_decay of the buffered head
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
     const T *xg = reinterpret_cast<const T *>(p.x);
     const T *bg = reinterpret_cast<const T *>(p.B);
     const T *cg = reinterpret_cast<const T *>(p.C);
-    const T *h16 = reinterpret_cast<const T *>(p.states16);
+    const T *h16 = reinterpret_cast<const T *>(p.prev);
 
     // ---- C_i fragments of the wave's tiles (register loads, once).
     Frag<T> cf[MAXIT][KS];
@@ -255,14 +254,16 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
         }
     }
 
-    // ---- phase B: heads.
-    const float dh_unused = 0.f;
-    (void)dh_unused;
+    // ---- phase B: heads.  Each wave waits for its own copies of head hh+1
+    // before it stores head hh's outputs (vmcnt counts stores too, so a wait
+    // placed after the stores would also wait for them to be written), and
+    // the barrier at the top of the next iteration then covers every wave's
+    // copies.
     T *yg = reinterpret_cast<T *>(p.y);
+    wait_vmcnt<0>();  // head 0's copies (and any ring leftovers) have landed
     for (int hh = 0; hh < hcnt; ++hh) {
         const int set = hh & 1;
-        wait_vmcnt<0>();   // this head's copies (and any ring leftovers) have landed
-        barrier_only();    // ... in every wave; the other buffer is no longer read
+        barrier_only();  // head hh is in buffer `set` for every wave; the other buffer is no longer read
         if (hh + 1 < hcnt) issue_head(hh + 1, set ^ 1);
 
         const int h = hbeg + hh;
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 
         // + D x (x_i from the head's LDS rows), round to bf16, store.
         const float dh = p.D ? p.D[h] : 0.f;
+        wait_vmcnt<0>();  // head hh+1's copies have landed (earlier stores are long done)
 #pragma unroll
         for (int k = 0; k < MAXIT; ++k) {
             const int i = 16 * tile[k] + il;
@@ -416,7 +418,6 @@ hipError_t dispatch_p(const Params &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream) {
-    if (!p.states16) return hipErrorNotSupported;
     switch (p.dstate) {
         case 16: return dispatch_p<1>(p, stream);
         case 32: return dispatch_p<2>(p, stream);

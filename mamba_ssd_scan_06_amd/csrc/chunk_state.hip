@@ -202,9 +202,10 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(Params p, bool at_inde
             const int pp = 16 * (wp * PTW + q) + il;
             f32x4 v = acc[a][q];
             if (at_index) {
-                const f32x4 hp = *reinterpret_cast<const f32x4 *>(p.states + state_base + (int64_t)pp * N + n);
+                const int64_t at = ((b * H + h) * (int64_t)P + pp) * N + n;
+                const f32x4 hp = *reinterpret_cast<const f32x4 *>(p.hj + at);
                 v = v + e_last * hp;
-                *reinterpret_cast<f32x4 *>(p.state_out + ((b * H + h) * (int64_t)P + pp) * N + n) = v;
+                *reinterpret_cast<f32x4 *>(p.state_out + at) = v;
             } else {
                 *reinterpret_cast<f32x4 *>(p.states + state_base + (int64_t)pp * N + n) = v;
             }

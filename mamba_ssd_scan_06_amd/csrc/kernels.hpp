@@ -7,6 +7,8 @@
 
 namespace ssd {
 
+enum class Elem { F32, BF16 };
+
 // Everything a kernel needs, passed by value.  Pointers are device pointers
 // with the layouts documented in include/ssd.h; `cs` and `states` point into
 // the caller's workspace.
@@ -25,19 +27,18 @@ struct Params {
     float *cs;                // workspace [b,H,nc,Q]: chunk-local cumulative log-decay
     float *dtc;               // workspace [b,H,nc,Q]: dt per chunk (0 past the end)
     float *dte;               // workspace [b,H,nc,Q]: dt_i * exp(cs_e - cs_i), e = last token of i's 32-token block
-    float *states;            // workspace [b,nc,H,P,N]: chunk states, then the state entering each chunk
-    void *states16;           // workspace [b,nc,H,P,N] bf16 copy of the state entering each chunk, or null
+    float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
+    void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
+    float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
 };
 
-enum class Elem { F32, BF16 };
-
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_chunk_cumsum(const Params &p, hipStream_t stream);
 hipError_t launch_chunk_state(const Params &p, Elem e, hipStream_t stream);
-hipError_t launch_state_pass(const Params &p, hipStream_t stream);
+hipError_t launch_state_pass(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // Head-batched bf16 chunk outputs; returns hipErrorNotSupported when the
 // shape does not fit its LDS budget (the caller then uses launch_chunk_output).

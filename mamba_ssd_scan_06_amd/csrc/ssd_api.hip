@@ -6,9 +6,9 @@
 // decomposition in section "SSD算法" of the "Transformers are SSMs" article):
 //   1. chunk_cumsum     dt, A            -> cs           (chunk-local log-decay)
 //   2. chunk_state      x, B, dt, cs     -> states[c]    (green: S_c from a zero start)
-//   3. state_pass       states, cs, h0   -> states[c] := h_{c-1}, final_state (yellow)
-//   4. chunk_output     x, B, C, dt, cs, states, D -> y  (orange + blue + D skip)
-//   5. state_at_index   (only with state_out) -> state_out
+//   3. state_pass       states, cs, h0   -> prev[c] = h_{c-1}, hj, final_state (yellow)
+//   4. chunk_output     x, B, C, cs, dt tables, prev, D -> y  (orange + blue + D skip)
+//   5. state_at_index   x, B, cs, dt, hj -> state_out  (only with state_out)
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -67,22 +67,24 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, dtc_off, dte_off, st_off, st16_off, total;
+    size_t cs_off, dtc_off, dte_off, st_off, prev_off, hj_off, total;
     int64_t nc;
 };
 
 Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     Layout L;
     L.nc = (s->seqlen + chunk - 1) / chunk;
+    const size_t esz = dtype == SSD_DTYPE_BF16 ? 2 : 4;
     const size_t tab_bytes = round_up((size_t)s->batch * s->nheads * L.nc * chunk * sizeof(float));
     const size_t n_st = (size_t)s->batch * L.nc * s->nheads * s->headdim * s->dstate;
+    const size_t n_hj = (size_t)s->batch * s->nheads * s->headdim * s->dstate;
     L.cs_off = 0;
     L.dtc_off = tab_bytes;
     L.dte_off = 2 * tab_bytes;
     L.st_off = 3 * tab_bytes;
-    L.st16_off = dtype == SSD_DTYPE_BF16 ? L.st_off + round_up(n_st * sizeof(float)) : 0;
-    const size_t end = dtype == SSD_DTYPE_BF16 ? L.st16_off + round_up(n_st * 2) : L.st_off + round_up(n_st * 4);
-    L.total = L.nc > 0 ? end : 0;
+    L.prev_off = L.st_off + round_up(n_st * sizeof(float));
+    L.hj_off = L.prev_off + round_up(n_st * esz);
+    L.total = L.nc > 0 ? L.hj_off + round_up(n_hj * sizeof(float)) : 0;
     return L;
 }
 
@@ -147,7 +149,8 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     out->dt_offset = L.dtc_off;
     out->dt_decay_offset = L.dte_off;
     out->states_offset = L.st_off;
-    out->states16_offset = L.st16_off;
+    out->prev_offset = L.prev_off;
+    out->hj_offset = L.hj_off;
     out->total_bytes = L.total;
     out->nchunks = L.nc;
     return SSD_OK;
@@ -223,7 +226,8 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.dtc = ws ? reinterpret_cast<float *>(ws + L.dtc_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
     p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
-    p.states16 = ws && dtype == SSD_DTYPE_BF16 ? static_cast<void *>(ws + L.st16_off) : nullptr;
+    p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;
+    p.hj = ws && state_out ? reinterpret_cast<float *>(ws + L.hj_off) : nullptr;
     p.batch = b;
     p.seqlen = T;
     p.nheads = (int)H;
@@ -244,7 +248,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
         run.step("chunk_state", [&] { return ssd::launch_chunk_state(p, e, stream); });
-        run.step("state_pass", [&] { return ssd::launch_state_pass(p, stream); });
+        run.step("state_pass", [&] { return ssd::launch_state_pass(p, e, stream); });
         run.step("chunk_output", [&] {
             if (e == ssd::Elem::BF16) {
                 const hipError_t r = ssd::launch_chunk_output_heads(p, stream);

@@ -7,15 +7,20 @@
 // true initial state.  With S_c the state chunk c reaches from a zero start
 // and a_c = exp(cs[c][Q-1]) its decay:
 //     h_{-1} = init_state (or 0),   h_c = a_c * h_{c-1} + S_c.
-// The kernel overwrites S_c with h_{c-1} (the state entering chunk c) and
-// writes h_{nc-1} to final_state.  For bf16 inputs it also stores h_{c-1}
-// rounded to bf16 (to nearest even), the form in which the output kernel
-// feeds it to the matrix cores.
+// The scan runs in fp32.  It writes
+//   prev[c] = h_{c-1}, rounded (to nearest even) to the input type, the form
+//             in which the output kernel feeds it to the matrix cores; chunk 0
+//             only when there is an initial state (otherwise it is zero and
+//             never read);
+//   hj      = h_{c_j-1} in fp32 for c_j = the chunk of state_out_idx[b], when
+//             the state at that index is requested;
+//   final_state = h_{nc-1}.
+// The chunk states themselves are left as they are.
 //
 // One lane per four consecutive state elements (b, h, p, n..n+3): 16-byte
-// coalesced loads and stores, sequential over chunks.  The chunk states of a
-// batch of chunks are loaded before any is overwritten so that the loads
-// are in flight together.
+// coalesced loads, sequential over chunks.  The chunk states of a batch of
+// chunks are loaded before any result is stored so that the loads are in
+// flight together.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +29,18 @@ namespace {
 
 constexpr int kBatchChunks = 8;
 
+template <typename T>
+__device__ inline void store4(T *dst, const f32x4 &v);
+template <>
+__device__ inline void store4<float>(float *dst, const f32x4 &v) {
+    *reinterpret_cast<f32x4 *>(dst) = v;
+}
+template <>
+__device__ inline void store4<bf16>(bf16 *dst, const f32x4 &v) {
+    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+template <typename T>
 __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
     const int64_t pn4 = (int64_t)p.headdim * p.dstate / 4;
     const int64_t per_b = (int64_t)p.nheads * pn4;
@@ -38,25 +55,33 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
     f32x4 hc = f32x4{0.f, 0.f, 0.f, 0.f};
     if (p.init_state) hc = reinterpret_cast<const f32x4 *>(p.init_state)[e];
     const float *cs_last = p.cs + (b * H + h) * (int64_t)nc * Q + (Q - 1);
-    f32x4 *st = reinterpret_cast<f32x4 *>(p.states);
+    const int64_t first = (b * nc * H + h) * pn4 + q;  // chunk 0's element, in units of 4
+    const int64_t stride = (int64_t)H * pn4;           // one chunk further
+    const f32x4 *st = reinterpret_cast<const f32x4 *>(p.states) + first;
+    T *prev = reinterpret_cast<T *>(p.prev) + 4 * first;
+    int cj = -1;  // chunk whose entering state the state-at-index step reads
+    if (p.hj && p.state_out_idx) {
+        const int j = p.state_out_idx[b];
+        cj = j < 0 ? -1 : (int)(min((int64_t)j, p.seqlen - 1) / Q);
+    }
 
+#pragma unroll 1
     for (int c0 = 0; c0 < nc; c0 += kBatchChunks) {
         f32x4 s[kBatchChunks];
         float a[kBatchChunks];
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             if (c0 + k < nc) {
-                s[k] = st[((b * nc + c0 + k) * H + h) * pn4 + q];
+                s[k] = st[(c0 + k) * stride];
                 a[k] = exp_neg(cs_last[(int64_t)(c0 + k) * Q]);
             }
         }
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
-            if (c0 + k < nc) {
-                const int64_t at = ((b * nc + c0 + k) * H + h) * pn4 + q;
-                st[at] = hc;
-                if (p.states16)
-                    reinterpret_cast<bf16x4 *>(p.states16)[at] = bf16x4{(bf16)hc[0], (bf16)hc[1], (bf16)hc[2], (bf16)hc[3]};
+            const int c = c0 + k;
+            if (c < nc) {
+                if (c > 0 || p.init_state) store4<T>(prev + 4 * c * stride, hc);
+                if (c == cj) reinterpret_cast<f32x4 *>(p.hj)[e] = hc;
                 hc = a[k] * hc + s[k];
             }
         }
@@ -77,10 +102,13 @@ __global__ __launch_bounds__(256) void empty_sequence_kernel(Params p) {
 
 }  // namespace
 
-hipError_t launch_state_pass(const Params &p, hipStream_t stream) {
+hipError_t launch_state_pass(const Params &p, Elem e, hipStream_t stream) {
     const int64_t n4 = p.batch * p.nheads * (int64_t)p.headdim * p.dstate / 4;
     const unsigned blocks = (unsigned)((n4 + 255) / 256);
-    hipLaunchKernelGGL(state_pass_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    if (e == Elem::BF16)
+        hipLaunchKernelGGL(state_pass_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(state_pass_kernel<float>, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

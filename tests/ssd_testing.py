@@ -68,8 +68,8 @@ def gpu_run(inp, chunk=None, use_D=True, use_init=True, use_state_out=True, dev=
     torch.cuda.synchronize()
     out = dict(y=to_np(y), final=to_np(fin), state_out=to_np(sout))
     if return_workspace:
-        cs, st = ssd.workspace_views(ws, shape, chunk, code)
-        out["cs"], out["states"] = to_np(cs), to_np(st)
+        cs, st, prev = ssd.workspace_views(ws, shape, chunk, code)
+        out["cs"], out["states"], out["prev"] = to_np(cs), to_np(st), to_np(prev)
     return out
 
 

@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 1
+    assert ssd.ssd_abi_version() == 2
 
 
 # ----------------------------------------------------------- full workloads
@@ -72,13 +72,21 @@ def test_step_chunk_cumsum(wl):
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
 def test_step_chunk_states_and_passing(wl):
-    # After the call the workspace holds, for every chunk, the state entering
-    # it: the chunk states (green) passed through the scan over chunks (yellow).
+    # After the call the workspace holds each chunk's state from a zero start
+    # (green) and the state entering each chunk (yellow, the scan over chunks).
     announce(f"chunk states {wl}")
     inp = ssd_inputs.generate(wl)
     got = gpu_run(inp, return_workspace=True)
     ref = oracle_run(inp, chunk=wl.chunk)
-    check("states entering each chunk", got["states"], ref["chunk_states"], TOL[wl.dtype])
+    Q, T = wl.chunk, wl.seqlen
+    zero_start = []
+    for t0 in range(0, T, Q):
+        sl = slice(t0, min(t0 + Q, T))
+        _, fin, _, _ = oracle.ssd_forward(inp.x[:, sl], inp.dt[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl])
+        zero_start.append(fin)
+    check("chunk states from a zero start", got["states"], np.stack(zero_start, axis=1), TOL[wl.dtype])
+    first = 0 if wl.init_state else 1  # entry 0 is written only with an initial state
+    check("states entering each chunk", got["prev"][:, first:], ref["chunk_states"][:, first:], TOL[wl.dtype])
     check("final_state", got["final"], ref["final"], TOL[wl.dtype])
 
 
