@@ -94,7 +94,8 @@ typedef struct {
  *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
  *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
  *            past seqlen count as dt = 0.
- *   dt       fp32, same layout: dt per chunk (0 past seqlen).
+ *   ct       fp32, same layout: cs * log2(e) - log2(dt) (+inf past seqlen),
+ *            so that dt_j exp(cs_i - cs_j) = exp2(cs_i log2(e) - ct_j).
  *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
  *            (within seqlen) of the 32-token block holding i.
  *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: entry c is the
@@ -106,7 +107,7 @@ typedef struct {
  *            chunk that holds state_out_idx[b] (written only with state_out). */
 typedef struct {
     size_t cumsum_offset;
-    size_t dt_offset;
+    size_t ct_offset;
     size_t dt_decay_offset;
     size_t states_offset;
     size_t prev_offset;

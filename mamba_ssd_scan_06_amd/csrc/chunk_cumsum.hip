@@ -12,7 +12,8 @@
 //
 // Two companion tables in the same [b,H,nc,Q] layout let the output kernel
 // copy a head's per-token factors of one chunk with contiguous loads:
-//   dtc[i] = dt_i (0 past the end of the sequence)
+//   ct[i]  = cs_i * log2(e) - log2(dt_i) (+inf past the end of the sequence),
+//            so that dt_j exp(cs_i - cs_j) = exp2(cs_i log2(e) - ct_j);
 //   dte[i] = dt_i * exp(cs_e - cs_i), e = the last token (within the
 //            sequence) of i's 32-token block; e >= i, so the factor is <= 1.
 //
@@ -30,6 +31,7 @@ namespace {
 
 constexpr int kHeads = 4;   // heads (waves) per workgroup
 constexpr int kBlock = 32;  // token block of dte
+constexpr double kLog2eD = 1.4426950408889634074;
 
 __device__ inline double shfl_up_f64(double v, int delta, int lane) {
     const int src = lane >= delta ? lane - delta : lane;
@@ -102,18 +104,20 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
     }
 
     const double a = (double)p.A[h];
-    typename FVec<VPT>::type csv, dtcv, dtev;
+    typename FVec<VPT>::type csv, ctv, dtev;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
+        const bool in = i0 + v < Qc;
         const float cs_i = (float)(a * s[v]);
-        const float de = i0 + v < Qc ? dtv[v] * exp_neg((float)(a * (se - s[v]))) : 0.f;
+        const float ct = in ? (float)(a * s[v] * kLog2eD) - log2f(dtv[v]) : __builtin_inff();
+        const float de = in ? dtv[v] * exp_neg((float)(a * (se - s[v]))) : 0.f;
         if constexpr (VPT == 1) {
             csv = cs_i;
-            dtcv = dtv[v];
+            ctv = ct;
             dtev = de;
         } else {
             csv[v] = cs_i;
-            dtcv[v] = dtv[v];
+            ctv[v] = ct;
             dtev[v] = de;
         }
     }
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
         typedef typename FVec<VPT>::type FV;
         const int64_t row = ((b * H + h) * nc + c) * (int64_t)Q + i0;
         *reinterpret_cast<FV *>(p.cs + row) = csv;
-        *reinterpret_cast<FV *>(p.dtc + row) = dtcv;
+        *reinterpret_cast<FV *>(p.ct + row) = ctv;
         *reinterpret_cast<FV *>(p.dte + row) = dtev;
     }
 }

@@ -15,28 +15,38 @@
 // heads of section "研究贡献") therefore share it: a workgroup owns
 // (b, c, g, a slice of the group's heads), computes the causal tiles of
 // G^T[j][i] = B_j . C_i once into registers (phase A), and then runs over its
-// heads, each head only masking/scaling G^T and multiplying by x (phase B).
+// heads, each head only scaling G^T and multiplying by x (phase B).
 //
 // Work split.  The chunk's 16-token column tiles ("i-tiles") are dealt to
-// W = tiles/2 waves, wave w owning tiles w and tiles-1-w, so that every wave
-// holds the same number of causal (i-tile, 32-token j block) pairs
-// (tiles/2 + 1).  Per pair a wave keeps two 16x16 tiles of G^T, rounded to
-// bf16 (nearest even) to fit the register budget; the decay-scaled value is
-// rounded to bf16 once more as the second product's operand.
+// W = tiles/2 waves, wave w owning tiles w and tiles-1-w, so every wave holds
+// the same number of causal (i-tile, 32-token j block) pairs.  Tile t meets
+// the j blocks m < t/2 wholly before it ("off-diagonal") and block t/2, which
+// holds its diagonal.  A wave walks the j blocks once per head: each block's
+// x^T fragments are read from LDS once and feed the pairs of both its tiles.
+// The G^T values of a pair are kept in registers rounded to bf16 (nearest
+// even); the decay-scaled value is rounded to bf16 once more as the second
+// product's operand.
 //
-// Data movement (gfx950 direct global -> LDS copies, no register staging):
-//  - phase A streams B through a ring of 32-token steps, several in flight;
-//  - phase B double-buffers whole heads: while head k computes, head k+1's x
-//    rows, bf16 initial state and per-token tables (cs, dt, dt_decay) land
-//    in the other buffer.
-// Tiles are stored unpadded with XOR swizzles so that the 16-byte-per-lane
-// reads (B, h) and the transposing reads (x) are spread over all LDS banks.
+// Decay factors (per head, from the cumsum tables):
+//  - off-diagonal block m, e = its last token:
+//        exp(cs_i - cs_j) dt_j = exp2(cs2_i - cs2_e) * dte_j,
+//    with cs2 = cs * log2(e) and dte_j = dt_j exp(cs_e - cs_j) (both factors <= 1);
+//  - diagonal block: exp(cs_i - cs_j) dt_j = exp2(cs2_i - ct_j),
+//    ct_j = cs2_j - log2(dt_j) (+inf where dt = 0); the causal mask j <= i is
+//    applied to the block's G^T values once, in phase A.
 //
-// Decay factors: for a j block wholly before the i-tile,
-//     exp(cs_i - cs_j) dt_j = exp(cs_i - cs_e) * dte_j,   e = last token of the block,
-// with dte_j = dt_j exp(cs_e - cs_j) precomputed by the cumsum kernel (both
-// factors <= 1); for the block holding the tile's diagonal the masked
-// difference is exponentiated directly (mask before exp).
+// Data movement:
+//  - phase A reads B fragments straight from global memory (L2);
+//  - phase B (gfx950 direct global -> LDS copies, no register staging) keeps whole heads in three buffers (two where LDS is short):
+//    while head k computes, the copies of head k+2 (x rows, bf16 initial
+//    state, per-token tables cs, ct, dte) are in flight and head k+1's have
+//    landed.  Each wave waits for its own copies of head k+1 before it stores
+//    head k's outputs (vmcnt counts stores too, so a wait after the stores
+//    would also wait for them to be written); the barrier that opens the
+//    next head then covers every wave's copies.
+// Tiles are stored unpadded with XOR swizzles of their 16-byte pieces so that
+// the 16-byte-per-lane reads of h and the transposing reads of x (four rows
+// of 32 bytes per 16 lanes) use all LDS banks.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -46,28 +56,40 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kStep = 32;  // tokens per j block
 
+// Piece swizzle of an x row of W 16-byte pieces for the transposing reads
+// (per 16 lanes: four rows, one 32-byte column pair each).
+template <int W>
+__device__ __forceinline__ int xsw(int r) {
+    return swz_tr<W>(r);
+}
+
 template <int NT, int PT, int NIT>
 struct HeadsCfg {
     static constexpr int N = NT * 16, P = PT * 16;
     static constexpr int KS = (N + 31) / 32, NP = KS * 32;
-    static constexpr int WB = NP / 8, WX = P / 8;              // 16-byte pieces per B / h row, per x row
+    static constexpr int WB = NP / 8, WX = P / 8;              // 16-byte pieces per h row, per x row
     static constexpr int W = NIT >= 2 ? NIT / 2 : 1;            // waves
     static constexpr int THREADS = 64 * W;
     static constexpr int MAXIT = NIT >= 2 ? 2 : 1;              // i-tiles per wave
-    static constexpr int NPAIR = NIT >= 2 ? NIT / 2 + 1 : 1;    // (i-tile, j block) pairs per wave
+    static constexpr int NBLK = NIT >= 2 ? W : 1;               // j blocks a wave visits at most
+    static constexpr int S0 = NIT >= 4 ? (W - 1) / 2 : 0;       // off-diagonal blocks of tile 0, at most
+    static constexpr int S1 = NIT >= 2 ? W - 1 : 0;             //   of tile 1, at most
+    static constexpr int U1 = NIT >= 4 ? W / 2 : 0;             //   of tile 1, at least
     static constexpr int QP = NIT * 16 < kStep ? kStep : NIT * 16;  // token rows held per head
     static constexpr int XE = QP * P;                           // x elements per head buffer
     static constexpr int HE = P * NP;                           // initial-state elements per head buffer
-    static constexpr int RSLOT = kStep * NP;                    // elements per B ring slot
-    static constexpr int RING = XE >= 4 * RSLOT ? 4 : 2;        // B ring slots (phase A, in x buffer 1)
-    static constexpr int X1E = XE > RING * RSLOT ? XE : RING * RSLOT;
     static constexpr int IXH = QP * WX / 64;                    // 1 KB copies per head: x rows
     static constexpr int IHH = P * WB / 64;                     //   initial-state rows
-    static constexpr int IHEAD = IXH + IHH + 3;                 //   + cs, dt, dt_decay tables
-    static constexpr int IHEAD_W = (IHEAD + W - 1) / W;
-    static constexpr int IB = kStep * WB / 64;                  // 1 KB copies per B step
-    static constexpr int IB_W = (IB + W - 1) / W;
-    static constexpr size_t LDS_BYTES = (size_t)(XE + X1E + 2 * HE + 512) * 2 + 2 * 3 * 256 * 4;
+    static constexpr int UX = (IXH + W - 1) / W;                // copies per wave per head: x
+    static constexpr int UH = (IHH + W - 1) / W;                //   initial state
+    static constexpr int UT = (3 + W - 1) / W;                  //   tables
+    static constexpr size_t lds_bytes(int nbuf) {
+        return (size_t)nbuf * ((XE + HE) * 2 + 3 * 256 * 4) + 512 * 2;
+    }
+    // Head buffers: three (copies run two heads ahead) when they fit in LDS
+    // and one head's copies per wave fit the vmcnt counter.
+    static constexpr int NBUF = lds_bytes(3) <= 160 * 1024 && UX + UH + UT < 64 ? 3 : 2;
+    static constexpr size_t LDS_BYTES = lds_bytes(NBUF);
 };
 
 template <int NT, int PT, int NIT>
@@ -76,14 +98,32 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
     using Cf = HeadsCfg<NT, PT, NIT>;
     using T = bf16;
     constexpr int N = Cf::N, P = Cf::P, KS = Cf::KS, NP = Cf::NP, WB = Cf::WB, WX = Cf::WX, W = Cf::W;
-    constexpr int MAXIT = Cf::MAXIT, NPAIR = Cf::NPAIR, RING = Cf::RING;
+    constexpr int MAXIT = Cf::MAXIT, NBLK = Cf::NBLK, S0 = Cf::S0, S1 = Cf::S1, U1 = Cf::U1;
+    constexpr int NBUF = Cf::NBUF, XE = Cf::XE, HE = Cf::HE;
     typedef typename Vec4<T>::type V4;
 
-    __shared__ __align__(16) T xs[Cf::XE + Cf::X1E];  // head buffers 0 and 1; the B ring in buffer 1 during phase A
-    T *const xs1 = xs + Cf::XE;
-    __shared__ __align__(16) T hs[2][Cf::HE];
-    __shared__ __align__(16) float tab[2][3][256];  // cs, dt, dt_decay of the buffered head
-    __shared__ __align__(16) T junk[512];           // target of padding copies (never read)
+    // Head buffers, one LDS object each: accesses to different objects carry
+    // different alias scopes, so reading one buffer while copies into another
+    // are in flight needs no wait for those copies.
+    __shared__ __align__(16) T xb0[XE], xb1[XE], xb2[NBUF == 3 ? XE : 8];
+    __shared__ __align__(16) T hb0[HE], hb1[HE], hb2[NBUF == 3 ? HE : 8];
+    __shared__ __align__(16) float tb0[3 * 256], tb1[3 * 256], tb2[NBUF == 3 ? 3 * 256 : 4];  // cs, ct, dte
+    __shared__ __align__(16) T junk[512];  // target of padding copies (never read)
+    auto xbuf = [&](auto bc) __attribute__((always_inline)) -> T * {
+        if constexpr (decltype(bc)::value == 0) return xb0;
+        else if constexpr (decltype(bc)::value == 1) return xb1;
+        else return xb2;
+    };
+    auto hbuf = [&](auto bc) __attribute__((always_inline)) -> T * {
+        if constexpr (decltype(bc)::value == 0) return hb0;
+        else if constexpr (decltype(bc)::value == 1) return hb1;
+        else return hb2;
+    };
+    auto tbuf = [&](auto bc) __attribute__((always_inline)) -> float * {
+        if constexpr (decltype(bc)::value == 0) return tb0;
+        else if constexpr (decltype(bc)::value == 1) return tb1;
+        else return tb2;
+    };
 
     const int Q = p.chunk, H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
     const int64_t L = p.seqlen;
@@ -103,24 +143,27 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
-    const int il = lane & 15, grp = lane >> 4, sl = lane & 15;
+    const int il = lane & 15, grp = lane >> 4;
     const int64_t t0 = (int64_t)c * Q;
     const int Qc = (int)(L - t0 < Q ? L - t0 : Q);
     const int nit = (Qc + 15) / 16;
     const bool has_prev = c > 0 || p.init_state != nullptr;
 
-    int tile[MAXIT];
+    // The wave's tiles, their diagonal blocks, and whether they hold tokens.
+    int tile[MAXIT], md[MAXIT];
+    bool live[MAXIT];
     tile[0] = wave;
     if constexpr (MAXIT == 2) tile[1] = NIT - 1 - wave;
-    const int n0 = tile[0] / 2 + 1;  // pairs of tile 0; pairs n0.. belong to tile 1
-    // pair u -> (slot k, j block m); wave-uniform
-    auto pair_k = [&](int u) { return (MAXIT == 1 || u < n0) ? 0 : 1; };
-    auto pair_m = [&](int u) { return u < n0 ? u : u - n0; };
+#pragma unroll
+    for (int k = 0; k < MAXIT; ++k) {
+        md[k] = tile[k] >> 1;
+        live[k] = tile[k] < nit;
+    }
 
     const T *xg = reinterpret_cast<const T *>(p.x);
     const T *bg = reinterpret_cast<const T *>(p.B);
     const T *cg = reinterpret_cast<const T *>(p.C);
-    const T *h16 = reinterpret_cast<const T *>(p.prev);
+    const T *hg = reinterpret_cast<const T *>(p.prev);
 
     // ---- C_i fragments of the wave's tiles (register loads, once).
     Frag<T> cf[MAXIT][KS];
@@ -136,140 +179,191 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
                 cf[k][ks].zero();
         }
     }
-    wait_vmcnt<0>();  // the copy pipelines below count only their own loads
 
-    // ---- copies of one head into buffer `set`.  Token rows past the chunk
+    // ---- copies of one head into buffer `bc`.  Token rows past the chunk
     // read its last token (in bounds, finite; their products meet an exact
-    // zero); dstate 16 fills each 32-column state row with two copies.
-    auto issue_head = [&](int hh, int set) {
+    // zero); dstate 16 fills each 32-column state row with two copies.  Every
+    // wave issues the same number of copies per head (padding copies go to
+    // `junk`), so a wave can wait for all but the last head's copies.
+    auto issue_head = [&](int hh, auto bc) __attribute__((always_inline)) {
         const int h = hbeg + hh;
         const T *xsrc = xg + ((b * L + t0) * H + h) * P;
-        const T *hsrc = h16 + (((b * nc + c) * H + h) * (int64_t)P) * N;
-        const int64_t trow = ((b * H + h) * nc + c) * (int64_t)Q;
-        T *xdst = xs + set * Cf::XE;
+        T *xdst = xbuf(bc);
 #pragma unroll
-        for (int u = 0; u < Cf::IHEAD_W; ++u) {
+        for (int u = 0; u < Cf::UX; ++u) {
             const int ins = wave + W * u;
-            if (ins < Cf::IXH) {
+            if (Cf::IXH % W == 0 || ins < Cf::IXH) {
                 const int U = 64 * ins + lane;
                 const int row = U / WX, pos = U - row * WX;
                 const int j = min(row, Qc - 1);
-                copy16_to_lds(xsrc + (int64_t)j * H * P + 8 * (pos ^ swz_tr<WX>(row)), xdst + ins * 512);
-            } else if (ins < Cf::IXH + Cf::IHH) {
-                if (has_prev) {
-                    const int U = 64 * (ins - Cf::IXH) + lane;
-                    const int row = U / WB, pos = U - row * WB;
-                    int gc = pos ^ swz_rows16<WB>(row);
-                    if constexpr (NP != N) gc %= N / 8;
-                    copy16_to_lds(hsrc + row * N + 8 * gc, &hs[set][(ins - Cf::IXH) * 512]);
-                } else {
-                    copy16_to_lds(xsrc, junk);
-                }
-            } else if (ins < Cf::IHEAD) {
-                const int t = ins - Cf::IXH - Cf::IHH;
-                const float *src = t == 0 ? p.cs : (t == 1 ? p.dtc : p.dte);
-                copy16_to_lds(src + trow + 4 * min(lane, Q / 4 - 1), &tab[set][t][0]);
+                copy16_to_lds(xsrc + (int64_t)j * H * P + 8 * (pos ^ xsw<WX>(row)), xdst + ins * 512);
             } else {
                 copy16_to_lds(xsrc, junk);
             }
         }
+        if (has_prev) {
+            const T *hsrc = hg + (((b * nc + c) * H + h) * (int64_t)P) * N;
+            T *hdst = hbuf(bc);
+#pragma unroll
+            for (int u = 0; u < Cf::UH; ++u) {
+                const int ins = wave + W * u;
+                if (Cf::IHH % W == 0 || ins < Cf::IHH) {
+                    const int U = 64 * ins + lane;
+                    const int row = U / WB, pos = U - row * WB;
+                    int gc = pos ^ swz_rows16<WB>(row);
+                    if constexpr (NP != N) gc %= N / 8;
+                    copy16_to_lds(hsrc + row * N + 8 * gc, hdst + ins * 512);
+                } else {
+                    copy16_to_lds(hsrc, junk);
+                }
+            }
+        }
+        // Per-token tables of this (b, h, c): one 1 KB row each (Q <= 256).
+        const int64_t trow = ((b * H + h) * nc + c) * (int64_t)Q;
+        const int lo = 4 * min(lane, Q / 4 - 1);
+        float *tdst = tbuf(bc);
+#pragma unroll
+        for (int u = 0; u < Cf::UT; ++u) {
+            const int t = wave + W * u;
+            if (t < 3) copy16_to_lds((t == 0 ? p.cs : (t == 1 ? p.ct : p.dte)) + trow + lo, tdst + 256 * t);
+            else copy16_to_lds(p.cs + trow, junk);
+        }
     };
 
-    // ---- phase A: causal tiles of G^T = B C^T, B streamed through the ring.
-    bf16x8 gt[NPAIR];  // slots 0-3: j tile 2m, slots 4-7: j tile 2m+1 (rows 4*grp + r)
+    // ---- phase A: causal tiles of G^T = B C^T.  B fragments come straight
+    // from global memory (each 32-token step of B is read by every wave, from
+    // L2 after the first), one step ahead of the products.
+    // go0/go1: off-diagonal blocks of tiles 0/1 (index = block), gd: diagonal
+    // blocks.  Lane (il, grp) holds G^T[j][i] for i = 16t + il and
+    // j = 32m + 4grp + r (slots 0-3) and j + 16 (slots 4-7).
+    bf16x8 go0[S0 > 0 ? S0 : 1], go1[S1 > 0 ? S1 : 1], gd[MAXIT];
+    const bf16x8 zero8 = {};
 #pragma unroll
-    for (int u = 0; u < NPAIR; ++u)
+    for (int s = 0; s < (S0 > 0 ? S0 : 1); ++s) go0[s] = zero8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gt[u][e] = (bf16)0.f;
+    for (int s = 0; s < (S1 > 0 ? S1 : 1); ++s) go1[s] = zero8;
+#pragma unroll
+    for (int k = 0; k < MAXIT; ++k) gd[k] = zero8;
 
     const T *bsrc = bg + ((b * L + t0) * G + g) * N;
-    auto issue_b = [&](int step, int slot) {
+    auto load_b = [&](int s, Frag<T> (&bf)[2][KS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < Cf::IB_W; ++u) {
-            const int ins = wave + W * u;
-            if (ins < Cf::IB) {
-                const int U = 64 * ins + lane;
-                const int row = U / WB, pos = U - row * WB;
-                int gc = pos ^ swz_rows16<WB>(row);
-                if constexpr (NP != N) gc %= N / 8;
-                const int j = min(kStep * step + row, Qc - 1);
-                copy16_to_lds(bsrc + (int64_t)j * G * N + 8 * gc, xs1 + slot * Cf::RSLOT + ins * 512);
-            } else {
-                copy16_to_lds(bsrc, junk);
+        for (int half = 0; half < 2; ++half) {
+            const int j = min(kStep * s + 16 * half + il, Qc - 1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int n0c = 32 * ks + 8 * grp;
+                if (n0c < N) load8(bf[half][ks], bsrc + (int64_t)j * G * N + n0c);
+                else bf[half][ks].zero();
             }
         }
     };
-    // Per-lane LDS offsets (elements).  Every swizzle here depends only on the
-    // row modulo a period that divides 16 (rows16) or 8 (tr), so a fragment's
-    // address is a per-lane constant plus a wave-uniform row offset.
-    //  - 16-byte-per-lane reads (B ring, h): row 16*a + il, piece 4*ks + grp.
+    // One step of phase A: the pair (tile K, block S).
+    auto pair_a = [&](auto kc, auto sc, const Frag<T> (&bfr)[2][KS]) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value, S = decltype(sc)::value;
+        if (!live[K] || S > md[K]) return;
+        const int t = tile[K];
+        const bool is_diag = S == md[K];
+        const int i = 16 * t + il;
+        bf16x8 v = zero8;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (2 * S + half > t) continue;  // above the diagonal
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma(bfr[half][ks], cf[K][ks], acc);
+            // The diagonal block keeps only j <= i (the causal mask, applied
+            // here once instead of per head).
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = kStep * S + 16 * half + 4 * grp + r;
+                v[4 * half + r] = (bf16)(is_diag && j > i ? 0.f : acc[r]);
+            }
+        }
+        // Value selects, not a branch between two destinations (that would
+        // turn into a store through a selected pointer and keep the arrays in
+        // scratch memory).
+        gd[K] = is_diag ? v : gd[K];
+        if constexpr (K == 0 && S < S0) go0[S] = is_diag ? go0[S] : v;
+        if constexpr (K == 1 && S < S1) go1[S] = is_diag ? go1[S] : v;
+    };
+
+    const int nstep = (Qc + kStep - 1) / kStep;
+    {
+        Frag<T> ba[2][KS], bb[2][KS];
+        load_b(0, ba);
+        issue_head(0, std::integral_constant<int, 0>{});
+        if (NBUF == 3 && hcnt > 1) issue_head(1, std::integral_constant<int, 1>{});
+        static_for<NBLK>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
+            if (s < nstep) {
+                auto step = [&](Frag<T> (&cur)[2][KS], Frag<T> (&nxt)[2][KS]) __attribute__((always_inline)) {
+                    if (s + 1 < nstep) load_b(s + 1, nxt);
+                    pair_a(std::integral_constant<int, 0>{}, sc, cur);
+                    if constexpr (MAXIT == 2) pair_a(std::integral_constant<int, 1>{}, sc, cur);
+                };
+                if constexpr (s % 2 == 0) step(ba, bb);
+                else step(bb, ba);
+            }
+        });
+    }
+
+    // Per-lane LDS offsets (elements).  Every swizzle depends only on the row
+    // modulo a period dividing 16, so a fragment's address is a per-lane
+    // constant plus a wave-uniform row offset.
+    //  - 16-byte-per-lane reads of h: row 16*a + il, piece 4*ks + grp.
     int roff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) roff[ks] = il * NP + 8 * ((4 * ks + grp) ^ swz_rows16<WB>(il));
-    //  - transposing reads of x: rows 32*m + 16*half + rl, columns 16*q + 4*(sl%4).
-    const int rl = 4 * grp + (sl >> 2);
+    //  - transposing reads of x: source lane (il = 4*kr + a) points at row
+    //    16*half + 4*grp + kr, columns 16*q + 4*a .. +3.
+    const int rl = 4 * grp + (il >> 2);
     int xoff[PT];
 #pragma unroll
-    for (int q = 0; q < PT; ++q) xoff[q] = rl * P + 16 * (q ^ (swz_tr<WX>(rl) >> 1)) + 4 * (sl & 3);
+    for (int q = 0; q < PT; ++q)
+        xoff[q] = rl * P + 8 * ((2 * q + ((il & 3) >> 1)) ^ xsw<WX>(rl)) + 4 * (il & 1);
     //  - D x reads: row i = 16*t + il, columns 16*q + 4*grp .. +3.
     int dxoff[PT];
 #pragma unroll
-    for (int q = 0; q < PT; ++q)
-        dxoff[q] = il * P + 8 * ((2 * q + (grp >> 1)) ^ swz_tr<WX>(il)) + 4 * (grp & 1);
+    for (int q = 0; q < PT; ++q) dxoff[q] = il * P + 8 * ((2 * q + (grp >> 1)) ^ xsw<WX>(il)) + 4 * (grp & 1);
 
-    issue_head(0, 0);
-    const int nstep = (Qc + kStep - 1) / kStep;
-#pragma unroll
-    for (int s = 0; s < RING - 1; ++s) issue_b(s, s);
-    for (int s = 0; s < nstep; ++s) {
-        wait_vmcnt<Cf::IB_W * (RING - 2)>();
-        barrier_only();
-        issue_b(s + RING - 1, (s + RING - 1) % RING);
-        const T *ring = xs1 + (s % RING) * Cf::RSLOT;
-        Frag<T> bfr[2][KS];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load8(bfr[half][ks], ring + 16 * half * NP + roff[ks]);
-#pragma unroll
-        for (int u = 0; u < NPAIR; ++u) {
-            if (pair_m(u) != s) continue;
-            auto body = [&](auto kc) {
-                constexpr int K = decltype(kc)::value;
-                const int t = tile[K];
-                if (t >= nit) return;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    if (2 * s + half > t) continue;  // above the diagonal
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) mma(bfr[half][ks], cf[K][ks], acc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) gt[u][4 * half + r] = (bf16)acc[r];
-                }
-            };
-            if (pair_k(u) == 0) body(std::integral_constant<int, 0>{});
-            else if constexpr (MAXIT == 2) body(std::integral_constant<int, 1>{});
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // ---- phase B: heads.  Each wave waits for its own copies of head hh+1
-    // before it stores head hh's outputs (vmcnt counts stores too, so a wait
-    // placed after the stores would also wait for them to be written), and
-    // the barrier at the top of the next iteration then covers every wave's
-    // copies.
+    // ---- phase B: heads; head hh lives in buffer hh % NBUF.
     T *yg = reinterpret_cast<T *>(p.y);
-    wait_vmcnt<0>();  // head 0's copies (and any ring leftovers) have landed
-    for (int hh = 0; hh < hcnt; ++hh) {
-        const int set = hh & 1;
-        barrier_only();  // head hh is in buffer `set` for every wave; the other buffer is no longer read
-        if (hh + 1 < hcnt) issue_head(hh + 1, set ^ 1);
+    // Per-lane output offsets within one head's rows: token i, channels 16q + 4grp.
+    uint32_t yoff[MAXIT];
+#pragma unroll
+    for (int k = 0; k < MAXIT; ++k) yoff[k] = (uint32_t)(16 * tile[k] + il) * (uint32_t)(H * P) + 4 * grp;
+
+    auto head = [&](auto bc, int hh) __attribute__((always_inline)) {
+        constexpr int BI = decltype(bc)::value;
+        // Head hh is in buffer BI for every wave, and no wave still reads the
+        // buffer of head hh-1, which now receives head hh+NBUF-1.
+        barrier_only();
+        const int ahead = hh + NBUF - 1;
+        // With three buffers, the first head of each loop iteration issues its
+        // copies after computing: the compiler's waitcnt state at the loop
+        // header no longer separates the buffers, so its LDS reads wait for
+        // every copy in flight, and those should then be old ones only.
+        constexpr bool late = NBUF == 3 && BI == 0;
+        if (!late && ahead < hcnt) issue_head(ahead, std::integral_constant<int, (BI + NBUF - 1) % NBUF>{});
 
         const int h = hbeg + hh;
-        const T *xsb = xs + set * Cf::XE;
-        const T *hsb = hs[set];
-        const float *csv = tab[set][0], *dtv = tab[set][1], *dtev = tab[set][2];
+        const T *xsb = xbuf(bc);
+        const T *hsb = hbuf(bc);
+        const float *csv = tbuf(bc), *ctv = csv + 256, *dtev = csv + 512;
+
+        float cs2i[MAXIT];
+#pragma unroll
+        for (int k = 0; k < MAXIT; ++k) cs2i[k] = csv[16 * tile[k] + il] * kLog2e;
+        // Keep G^T packed between heads: an empty asm makes the values opaque
+        // per head, so their bf16 -> fp32 unpacking is not hoisted out of the
+        // head loop (twice the registers, and spills).
+#pragma unroll
+        for (int s = 0; s < (S0 > 0 ? S0 : 1); ++s) asm volatile("" : "+v"(go0[s]));
+#pragma unroll
+        for (int s = 0; s < (S1 > 0 ? S1 : 1); ++s) asm volatile("" : "+v"(go1[s]));
+#pragma unroll
+        for (int k = 0; k < MAXIT; ++k) asm volatile("" : "+v"(gd[k]));
 
         f32x4 acc[MAXIT][PT];
 #pragma unroll
@@ -291,84 +385,118 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
             }
 #pragma unroll
             for (int k = 0; k < MAXIT; ++k) {
-                const int i = 16 * tile[k] + il;
-                const float ei = i < Qc ? exp_neg(csv[i]) : 0.f;
+                const float ei = exp2_hw(cs2i[k]);
 #pragma unroll
                 for (int q = 0; q < PT; ++q) acc[k][q] = acc[k][q] * ei;
             }
         }
 
-        // Orange: per (tile, j block) pair, mask/scale G^T and multiply by x.
+        // Orange: walk the j blocks; each block's x^T fragments serve both tiles.
+        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            const bool use0 = live[0] && m <= md[0];
+            const bool use1 = MAXIT == 2 && live[MAXIT - 1] && m <= md[MAXIT - 1];
+            if (!use0 && !use1) return;
+            const T *xm = xsb + kStep * m * P;
+            Frag<T> xf[PT];
 #pragma unroll
-        for (int u = 0; u < NPAIR; ++u) {
-            auto body = [&](auto kc) {
+            for (int q = 0; q < PT; ++q) {
+                const i16x4 a0 = ds_read_tr16(xm + xoff[q]);
+                const i16x4 a1 = ds_read_tr16(xm + 16 * P + xoff[q]);
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                xf[q].v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+            }
+            auto off_diag = [&](auto kc, const bf16x8 &gv) __attribute__((always_inline)) {
                 constexpr int K = decltype(kc)::value;
-                const int t = tile[K];
-                if (t >= nit) return;
-                const int m = pair_m(u);
-                const int i = 16 * t + il;
-                const float cs_i = csv[i];
+                const float ai = exp2_hw(cs2i[K] - csv[kStep * m + kStep - 1] * kLog2e);
+                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dtev + kStep * m + 4 * grp);
+                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dtev + kStep * m + 16 + 4 * grp);
                 Frag<T> lf;
-                if (kStep * m + kStep - 1 < 16 * t) {
-                    // whole block before the tile: exp(cs_i - cs_e) * dte_j
-                    const float ai = exp_neg(fminf(cs_i - csv[kStep * m + kStep - 1], 0.f));
-                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dtev + kStep * m + 4 * grp);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dtev + kStep * m + 16 + 4 * grp);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        lf.set(r, (float)gt[u][r] * (ai * d0[r]));
-                        lf.set(4 + r, (float)gt[u][4 + r] * (ai * d1[r]));
-                    }
-                } else {
-                    // block holding the diagonal: mask (j <= i) before exp
-                    const f32x4 c0 = *reinterpret_cast<const f32x4 *>(csv + kStep * m + 4 * grp);
-                    const f32x4 c1 = *reinterpret_cast<const f32x4 *>(csv + kStep * m + 16 + 4 * grp);
-                    const f32x4 t0v = *reinterpret_cast<const f32x4 *>(dtv + kStep * m + 4 * grp);
-                    const f32x4 t1v = *reinterpret_cast<const f32x4 *>(dtv + kStep * m + 16 + 4 * grp);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j0 = kStep * m + 4 * grp + r, j1 = j0 + 16;
-                        const float e0 = exp_neg(fminf(cs_i - c0[r], 0.f)) * t0v[r];
-                        const float e1 = exp_neg(fminf(cs_i - c1[r], 0.f)) * t1v[r];
-                        lf.set(r, j0 <= i ? (float)gt[u][r] * e0 : 0.f);
-                        lf.set(4 + r, j1 <= i ? (float)gt[u][4 + r] * e1 : 0.f);
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    lf.set(r, (float)gv[r] * (ai * d0[r]));
+                    lf.set(4 + r, (float)gv[4 + r] * (ai * d1[r]));
                 }
-                const T *xm = xsb + kStep * m * P;
 #pragma unroll
-                for (int q = 0; q < PT; ++q) {
-                    const i16x4 a0 = ds_read_tr16(xm + xoff[q]);
-                    const i16x4 a1 = ds_read_tr16(xm + 16 * P + xoff[q]);
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    Frag<T> xf;
-                    xf.v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-                    mma(xf, lf, acc[K][q]);
-                }
+                for (int q = 0; q < PT; ++q) mma(xf[q], lf, acc[K][q]);
             };
-            if (pair_k(u) == 0) body(std::integral_constant<int, 0>{});
-            else if constexpr (MAXIT == 2) body(std::integral_constant<int, 1>{});
-            // Keep the scheduler from hoisting later pairs' LDS reads over this
-            // one (their live ranges would exceed the register budget).
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            auto diag = [&](auto kc) __attribute__((always_inline)) {
+                constexpr int K = decltype(kc)::value;
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(ctv + kStep * m + 4 * grp);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(ctv + kStep * m + 16 + 4 * grp);
+                Frag<T> lf;
+                // gd is zero above the diagonal; there the exponent may be
+                // large, so it is capped to keep 0 * 2^x finite (below the
+                // diagonal it is at most log2(dt_j)).
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e0 = exp2_hw(fminf(cs2i[K] - c0[r], 64.f));
+                    const float e1 = exp2_hw(fminf(cs2i[K] - c1[r], 64.f));
+                    lf.set(r, (float)gd[K][r] * e0);
+                    lf.set(4 + r, (float)gd[K][4 + r] * e1);
+                }
+#pragma unroll
+                for (int q = 0; q < PT; ++q) mma(xf[q], lf, acc[K][q]);
+            };
+            if (use0) {
+                if constexpr (m < S0) {
+                    if (m < md[0]) off_diag(std::integral_constant<int, 0>{}, go0[m]);
+                    else diag(std::integral_constant<int, 0>{});
+                } else {
+                    diag(std::integral_constant<int, 0>{});
+                }
+            }
+            if constexpr (MAXIT == 2) {
+                if (use1) {
+                    if constexpr (m < U1) {
+                        off_diag(std::integral_constant<int, 1>{}, go1[m]);
+                    } else if constexpr (m < S1) {
+                        if (m < md[1]) off_diag(std::integral_constant<int, 1>{}, go1[m]);
+                        else diag(std::integral_constant<int, 1>{});
+                    } else {
+                        diag(std::integral_constant<int, 1>{});
+                    }
+                }
+            }
+        });
 
         // + D x (x_i from the head's LDS rows), round to bf16, store.
-        const float dh = p.D ? p.D[h] : 0.f;
-        wait_vmcnt<0>();  // head hh+1's copies have landed (earlier stores are long done)
+        if (late && ahead < hcnt) issue_head(ahead, std::integral_constant<int, (BI + NBUF - 1) % NBUF>{});
+
+        // D through the constant address space: a scalar load, which vmcnt
+        // does not count (a vector load here would have to wait for the copies).
+        const float dh = p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[h] : 0.f;
+        T *yh = yg + ((b * L + t0) * H + h) * P;
+        // Head hh+1's copies have landed: its loads precede the last head's
+        // in issue order and loads complete in order (pending older stores
+        // only make the wait stricter).
+        if (NBUF == 3 && ahead < hcnt) {
+            if (has_prev) wait_vmcnt<NBUF == 3 ? Cf::UX + Cf::UH + Cf::UT : 0>();
+            else wait_vmcnt<NBUF == 3 ? Cf::UX + Cf::UT : 0>();
+        } else {
+            wait_vmcnt<0>();
+        }
 #pragma unroll
         for (int k = 0; k < MAXIT; ++k) {
             const int i = 16 * tile[k] + il;
-            if (tile[k] >= nit || i >= Qc) continue;
-            const int64_t row = ((b * L + t0 + i) * H + h) * (int64_t)P;
+            if (!live[k] || i >= Qc) continue;
 #pragma unroll
             for (int q = 0; q < PT; ++q) {
                 const V4 xv = *reinterpret_cast<const V4 *>(xsb + 16 * tile[k] * P + dxoff[q]);
                 V4 out;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[r] = (T)(acc[k][q][r] + dh * (float)xv[r]);
-                *reinterpret_cast<V4 *>(yg + row + 16 * q + 4 * grp) = out;
+                *reinterpret_cast<V4 *>(yh + yoff[k] + 16 * q) = out;
             }
         }
+    };
+
+    wait_vmcnt<0>();  // the first heads' copies have landed
+    for (int h0 = 0; h0 < hcnt; h0 += NBUF) {
+        static_for<NBUF>([&](auto bc) __attribute__((always_inline)) {
+            const int hh = h0 + decltype(bc)::value;
+            if (hh < hcnt) head(bc, hh);
+        });
     }
     wait_vmcnt<0>();  // no copy outlives the workgroup
 }

@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace ssd {
 
@@ -38,6 +39,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // (decays); results below the fp32 normal range flush to zero, which is
 // below any output's resolution.
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// 2^x through the same hardware instruction (no range reduction: results
+// below the fp32 normal range flush to zero).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -192,5 +196,16 @@ template <> struct Vec8<float> { typedef float type __attribute__((ext_vector_ty
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (unrolled, with
+// compile-time indices, e.g. for register arrays).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace ssd

@@ -25,7 +25,7 @@ struct Params {
     float *final_state;       // [b,H,P,N] or null
     float *state_out;         // [b,H,P,N] or null
     float *cs;                // workspace [b,H,nc,Q]: chunk-local cumulative log-decay
-    float *dtc;               // workspace [b,H,nc,Q]: dt per chunk (0 past the end)
+    float *ct;                // workspace [b,H,nc,Q]: cs * log2(e) - log2(dt) (+inf past the end)
     float *dte;               // workspace [b,H,nc,Q]: dt_i * exp(cs_e - cs_i), e = last token of i's 32-token block
     float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)

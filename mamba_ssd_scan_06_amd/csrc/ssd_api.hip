@@ -4,7 +4,7 @@
 //
 // Launch sequence on the caller's stream (each step of the block
 // decomposition in section "SSD算法" of the "Transformers are SSMs" article):
-//   1. chunk_cumsum     dt, A            -> cs           (chunk-local log-decay)
+//   1. chunk_cumsum     dt, A            -> cs, ct, dte  (chunk-local log-decay tables)
 //   2. chunk_state      x, B, dt, cs     -> states[c]    (green: S_c from a zero start)
 //   3. state_pass       states, cs, h0   -> prev[c] = h_{c-1}, hj, final_state (yellow)
 //   4. chunk_output     x, B, C, cs, dt tables, prev, D -> y  (orange + blue + D skip)
@@ -67,7 +67,7 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, dtc_off, dte_off, st_off, prev_off, hj_off, total;
+    size_t cs_off, ct_off, dte_off, st_off, prev_off, hj_off, total;
     int64_t nc;
 };
 
@@ -79,7 +79,7 @@ Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     const size_t n_st = (size_t)s->batch * L.nc * s->nheads * s->headdim * s->dstate;
     const size_t n_hj = (size_t)s->batch * s->nheads * s->headdim * s->dstate;
     L.cs_off = 0;
-    L.dtc_off = tab_bytes;
+    L.ct_off = tab_bytes;
     L.dte_off = 2 * tab_bytes;
     L.st_off = 3 * tab_bytes;
     L.prev_off = L.st_off + round_up(n_st * sizeof(float));
@@ -146,7 +146,7 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     if (st != SSD_OK) return st;
     const Layout L = layout_of(shape, chunk_size, dtype);
     out->cumsum_offset = L.cs_off;
-    out->dt_offset = L.dtc_off;
+    out->ct_offset = L.ct_off;
     out->dt_decay_offset = L.dte_off;
     out->states_offset = L.st_off;
     out->prev_offset = L.prev_off;
@@ -223,7 +223,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.state_out = state_out;
     char *ws = static_cast<char *>(workspace);
     p.cs = ws ? reinterpret_cast<float *>(ws + L.cs_off) : nullptr;
-    p.dtc = ws ? reinterpret_cast<float *>(ws + L.dtc_off) : nullptr;
+    p.ct = ws ? reinterpret_cast<float *>(ws + L.ct_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
     p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
     p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;

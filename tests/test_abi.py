@@ -50,13 +50,13 @@ def shape(b=2, T=100, H=4, P=64, N=128, G=2):
 def test_workspace_bytes_formula():
     s = shape()
     nc = (100 + 63) // 64
-    tab = 2 * 4 * nc * 64 * 4                # cs, dt, dt_decay: fp32 [b,H,nc,Q] each
+    tab = 2 * 4 * nc * 64 * 4                # cs, ct, dt_decay: fp32 [b,H,nc,Q] each
     n_st = 2 * nc * 4 * 64 * 128             # states, prev: [b,nc,H,P,N]
     n_hj = 2 * 4 * 64 * 128                  # hj: [b,H,P,N]
     rnd = lambda v: (v + 255) // 256 * 256
     lay = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_BF16)
     assert lay.nchunks == nc and lay.cumsum_offset == 0
-    assert lay.dt_offset == rnd(tab) and lay.dt_decay_offset == 2 * rnd(tab)
+    assert lay.ct_offset == rnd(tab) and lay.dt_decay_offset == 2 * rnd(tab)
     assert lay.states_offset == 3 * rnd(tab)
     assert lay.prev_offset == lay.states_offset + rnd(4 * n_st)
     assert lay.hj_offset == lay.prev_offset + rnd(2 * n_st)
