@@ -50,7 +50,7 @@ KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
     "chunk_state": ["chunk_state.hip", "device_common.hpp"],
     "state_pass": ["state_pass.hip", "device_common.hpp"],
-    "chunk_output": ["chunk_output.hip", "device_common.hpp"],
+    "chunk_output": ["chunk_output_heads.hip", "chunk_output.hip", "device_common.hpp"],
     "state_at_index": ["chunk_state.hip", "device_common.hpp"],
 }
 CSRC = os.path.join(ROOT, "mamba_ssd_scan_06_amd", "csrc")
@@ -66,26 +66,28 @@ def chunk_lengths(wl):
 def algorithmic_work(wl, idx=None):
     """Minimal HBM bytes and algorithmic flops of each kernel for one call.
 
-    Bytes count each tensor a kernel must read or write once (inputs in their
-    dtype, states and workspace in fp32).  Flops count the causal triangle
-    only and C.B^T once per (b, chunk, group), not per head."""
+    Bytes count each tensor a kernel must read or write once: inputs in their
+    dtype, the per-token tables (cs, ct, dte) and chunk states in fp32, the
+    states entering each chunk in the input dtype.  Flops count the causal
+    triangle only and C.B^T once per (b, chunk, group), not per head."""
     b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
     e = 2 if wl.dtype == "bf16" else 4
     nc = len(chunk_lengths(wl))
     x = b * T * H * P * e
     bc = b * T * G * N * e
     dt = b * T * H * 4
-    cs = b * H * nc * wl.chunk * 4
-    st = b * H * P * N * 4               # one state per (b, h)
-    S = nc * st                          # one state per (b, chunk, h)
+    tab = b * H * nc * wl.chunk * 4      # one per-token table
+    st = b * H * P * N * 4               # one fp32 state per (b, h)
+    S = nc * st                          # chunk states, fp32
     prev_chunks = nc if wl.init_state else nc - 1
+    prev = prev_chunks * st // 4 * e     # states entering chunks, input dtype
     qs = chunk_lengths(wl)
     work = {
-        "chunk_cumsum": dict(bytes=dt + cs, flops=b * T * H),
-        "chunk_state": dict(bytes=x + bc + dt + cs + S, flops=2 * b * H * sum(qs) * N * P),
-        "state_pass": dict(bytes=2 * S + st + (st if wl.init_state else 0), flops=2 * b * nc * H * P * N),
+        "chunk_cumsum": dict(bytes=dt + 3 * tab, flops=b * T * H),
+        "chunk_state": dict(bytes=x + bc + dt + tab + S, flops=2 * b * H * sum(qs) * N * P),
+        "state_pass": dict(bytes=S + prev + st + (st if wl.init_state else 0), flops=2 * b * nc * H * P * N),
         "chunk_output": dict(
-            bytes=2 * x + 2 * bc + dt + cs + prev_chunks * st,
+            bytes=2 * x + 2 * bc + 3 * tab + prev,
             flops=b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P for q in qs)
             + 2 * b * H * N * P * sum(q for c, q in enumerate(qs) if c > 0 or wl.init_state)),
     }
@@ -183,19 +185,25 @@ def time_workload(wl, steps, warmup, device, events):
     kw = dict(y=y, final_state=fin, state_out=sout, workspace=ws)
     for _ in range(warmup):
         ssd.ssd_chunk_scan_fwd(*args, **kw)
-    nk = 5 if wl.state_out else 4
-    marks = [events.create(nk + 1) for _ in range(steps)]
+    # Whole steps, back to back, with events only around the timed region.
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
-    names = None
-    for k in range(steps):
-        _, _, _, names = ssd.ssd_chunk_scan_fwd_marked(*args, marks=marks[k], **kw)
+    for _ in range(steps):
+        ssd.ssd_chunk_scan_fwd(*args, **kw)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps
+    # Per-kernel durations: the same steps again, with HIP events recorded on
+    # the kernels' stream between kernels.
+    nk = 5 if wl.state_out else 4
+    marks = [events.create(nk + 1) for _ in range(steps)]
+    names = None
+    for k in range(steps):
+        _, _, _, names = ssd.ssd_chunk_scan_fwd_marked(*args, marks=marks[k], **kw)
+    torch.cuda.synchronize()
     per_kernel = {}
     for i, name in enumerate(names):
         per_kernel[name] = sum(events.elapsed_ms(m[i], m[i + 1]) for m in marks) / steps
@@ -308,6 +316,8 @@ def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
     copy_bytes = 256 << 20
 
     def find(d, key):
+        # kernel symbols look like "...chunk_output_heads_kernel<8, 4, 16>(...)"; the
+        # step's kernel is the matching one with the most dispatches
         hits = {k: v for k, v in d.items() if key in k}
         return max(hits.items(), key=lambda kv: len(kv[1])) if hits else (None, None)
 
@@ -320,8 +330,8 @@ def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
     wl = ssd_inputs.WORKLOADS[workload]
     work = algorithmic_work(wl)
     for kernel in ("chunk_output", "chunk_state", "state_pass", "chunk_cumsum"):
-        kf_name, kf = find(fetch, kernel + "_kernel")
-        _, kw = find(write, kernel + "_kernel")
+        kf_name, kf = find(fetch, kernel)
+        _, kw = find(write, kernel)
         if not kf or not kw:
             continue
         fb = sorted(kf)[len(kf) // 2] * 1024.0 * f_copy
