@@ -63,18 +63,21 @@ __device__ __forceinline__ int xsw(int r) {
     return swz_tr<W>(r);
 }
 
-template <int NT, int PT, int NIT>
+// WIDE: one i-tile per wave (NIT waves, at most 128 VGPRs, so four waves
+// share a SIMD); otherwise two tiles per wave (NIT/2 waves).
+template <int NT, int PT, int NIT, bool WIDE>
 struct HeadsCfg {
     static constexpr int N = NT * 16, P = PT * 16;
     static constexpr int KS = (N + 31) / 32, NP = KS * 32;
     static constexpr int WB = NP / 8, WX = P / 8;              // 16-byte pieces per h row, per x row
-    static constexpr int W = NIT >= 2 ? NIT / 2 : 1;            // waves
+    static constexpr int W = WIDE ? NIT : (NIT >= 2 ? NIT / 2 : 1);  // waves
     static constexpr int THREADS = 64 * W;
-    static constexpr int MAXIT = NIT >= 2 ? 2 : 1;              // i-tiles per wave
-    static constexpr int NBLK = NIT >= 2 ? W : 1;               // j blocks a wave visits at most
-    static constexpr int S0 = NIT >= 4 ? (W - 1) / 2 : 0;       // off-diagonal blocks of tile 0, at most
-    static constexpr int S1 = NIT >= 2 ? W - 1 : 0;             //   of tile 1, at most
-    static constexpr int U1 = NIT >= 4 ? W / 2 : 0;             //   of tile 1, at least
+    static constexpr int MAXIT = !WIDE && NIT >= 2 ? 2 : 1;     // i-tiles per wave
+    static constexpr int NBLK = NIT >= 2 ? NIT / 2 : 1;         // j blocks a wave visits at most
+    static constexpr int S0 = WIDE ? (NIT >= 2 ? NIT / 2 - 1 : 0)       // off-diagonal blocks of tile 0, at most
+                                   : (NIT >= 4 ? (W - 1) / 2 : 0);
+    static constexpr int S1 = !WIDE && NIT >= 2 ? W - 1 : 0;    //   of tile 1, at most
+    static constexpr int U1 = !WIDE && NIT >= 4 ? W / 2 : 0;    //   of tile 1, at least
     static constexpr int QP = NIT * 16 < kStep ? kStep : NIT * 16;  // token rows held per head
     static constexpr int XE = QP * P;                           // x elements per head buffer
     static constexpr int HE = P * NP;                           // initial-state elements per head buffer
@@ -88,14 +91,31 @@ struct HeadsCfg {
     }
     // Head buffers: three (copies run two heads ahead) when they fit in LDS
     // and one head's copies per wave fit the vmcnt counter.
-    static constexpr int NBUF = lds_bytes(3) <= 160 * 1024 && UX + UH + UT < 64 ? 3 : 2;
+    // (The one-tile-per-wave layout hides latency with four waves per SIMD
+    // and keeps two buffers: fewer per-buffer address registers.)
+    static constexpr int NBUF = !WIDE && lds_bytes(3) <= 160 * 1024 && UX + UH + UT < 64 ? 3 : 2;
     static constexpr size_t LDS_BYTES = lds_bytes(NBUF);
 };
 
-template <int NT, int PT, int NIT>
-__global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_heads_kernel(Params p, int hps,
-                                                                                           int nslices) {
-    using Cf = HeadsCfg<NT, PT, NIT>;
+// Tile of wave w in the one-tile-per-wave layout.  Waves w, w+4, w+8, w+12
+// share a SIMD; tile t meets t/2 + 1 causal blocks, and these orders give
+// every SIMD the same number.
+template <int NIT>
+__device__ __forceinline__ int wide_tile(int w) {
+    if constexpr (NIT == 16) {
+        constexpr unsigned long long map = 0xdcfeab894567'3210ull;  // nibble w = tile of wave w
+        return (int)((map >> (4 * w)) & 15);
+    } else if constexpr (NIT == 8) {
+        return w < 4 ? w : 11 - w;
+    } else {
+        return w;
+    }
+}
+
+template <int NT, int PT, int NIT, bool WIDE>
+__global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_heads_kernel(Params p, int hps,
+                                                                                                  int nslices) {
+    using Cf = HeadsCfg<NT, PT, NIT, WIDE>;
     using T = bf16;
     constexpr int N = Cf::N, P = Cf::P, KS = Cf::KS, NP = Cf::NP, WB = Cf::WB, WX = Cf::WX, W = Cf::W;
     constexpr int MAXIT = Cf::MAXIT, NBLK = Cf::NBLK, S0 = Cf::S0, S1 = Cf::S1, U1 = Cf::U1;
@@ -152,8 +172,12 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
     // The wave's tiles, their diagonal blocks, and whether they hold tokens.
     int tile[MAXIT], md[MAXIT];
     bool live[MAXIT];
-    tile[0] = wave;
-    if constexpr (MAXIT == 2) tile[1] = NIT - 1 - wave;
+    if constexpr (WIDE) {
+        tile[0] = wide_tile<NIT>(wave);
+    } else {
+        tile[0] = wave;
+        if constexpr (MAXIT == 2) tile[1] = NIT - 1 - wave;
+    }
 #pragma unroll
     for (int k = 0; k < MAXIT; ++k) {
         md[k] = tile[k] >> 1;
@@ -182,24 +206,51 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 
     // ---- copies of one head into buffer `bc`.  Token rows past the chunk
     // read its last token (in bounds, finite; their products meet an exact
-    // zero); dstate 16 fills each 32-column state row with two copies.  Every
-    // wave issues the same number of copies per head (padding copies go to
-    // `junk`), so a wave can wait for all but the last head's copies.
+    // zero); dstate 16 fills each 32-column state row with two copies.  A
+    // wave knows how many copies one head adds (padding copies go to `junk`;
+    // with three or more waves only waves 0-2 copy the three table rows), so
+    // it can wait for all but the last head's copies.
+    // Per-lane source offsets (elements) of the copies; the same for every
+    // head, whose base address is uniform.
+    uint32_t offx[Cf::UX], offh[Cf::UH];
+#pragma unroll
+    for (int u = 0; u < Cf::UX; ++u) {
+        const int U = 64 * (wave + W * u) + lane;
+        const int row = U / WX, pos = U - row * WX;
+        offx[u] = (uint32_t)min(row, Qc - 1) * (uint32_t)(H * P) + 8 * (pos ^ xsw<WX>(row));
+    }
+#pragma unroll
+    for (int u = 0; u < Cf::UH; ++u) {
+        const int U = 64 * (wave + W * u) + lane;
+        const int row = U / WB, pos = U - row * WB;
+        int gc = pos ^ swz_rows16<WB>(row);
+        if constexpr (NP != N) gc %= N / 8;
+        offh[u] = (uint32_t)(row * N + 8 * gc);
+    }
+    const uint32_t offt = 4 * min(lane, Q / 4 - 1);
+
     auto issue_head = [&](int hh, auto bc) __attribute__((always_inline)) {
         const int h = hbeg + hh;
+        // Opaque copies of the lane offsets: otherwise base + lane offset is
+        // reassociated and hoisted out of the head loop as 64-bit values.
+        uint32_t ox[Cf::UX], oh[Cf::UH];
+#pragma unroll
+        for (int u = 0; u < Cf::UX; ++u) {
+            ox[u] = offx[u];
+            asm volatile("" : "+v"(ox[u]));
+        }
+#pragma unroll
+        for (int u = 0; u < Cf::UH; ++u) {
+            oh[u] = offh[u];
+            asm volatile("" : "+v"(oh[u]));
+        }
         const T *xsrc = xg + ((b * L + t0) * H + h) * P;
         T *xdst = xbuf(bc);
 #pragma unroll
         for (int u = 0; u < Cf::UX; ++u) {
             const int ins = wave + W * u;
-            if (Cf::IXH % W == 0 || ins < Cf::IXH) {
-                const int U = 64 * ins + lane;
-                const int row = U / WX, pos = U - row * WX;
-                const int j = min(row, Qc - 1);
-                copy16_to_lds(xsrc + (int64_t)j * H * P + 8 * (pos ^ xsw<WX>(row)), xdst + ins * 512);
-            } else {
-                copy16_to_lds(xsrc, junk);
-            }
+            if (Cf::IXH % W == 0 || ins < Cf::IXH) copy16_to_lds(xsrc + ox[u], xdst + ins * 512);
+            else copy16_to_lds(xsrc, junk);
         }
         if (has_prev) {
             const T *hsrc = hg + (((b * nc + c) * H + h) * (int64_t)P) * N;
@@ -207,26 +258,20 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 #pragma unroll
             for (int u = 0; u < Cf::UH; ++u) {
                 const int ins = wave + W * u;
-                if (Cf::IHH % W == 0 || ins < Cf::IHH) {
-                    const int U = 64 * ins + lane;
-                    const int row = U / WB, pos = U - row * WB;
-                    int gc = pos ^ swz_rows16<WB>(row);
-                    if constexpr (NP != N) gc %= N / 8;
-                    copy16_to_lds(hsrc + row * N + 8 * gc, hdst + ins * 512);
-                } else {
-                    copy16_to_lds(hsrc, junk);
-                }
+                if (Cf::IHH % W == 0 || ins < Cf::IHH) copy16_to_lds(hsrc + oh[u], hdst + ins * 512);
+                else copy16_to_lds(hsrc, junk);
             }
         }
         // Per-token tables of this (b, h, c): one 1 KB row each (Q <= 256).
         const int64_t trow = ((b * H + h) * nc + c) * (int64_t)Q;
-        const int lo = 4 * min(lane, Q / 4 - 1);
+        uint32_t offt_h = offt;
+        asm volatile("" : "+v"(offt_h));
         float *tdst = tbuf(bc);
 #pragma unroll
         for (int u = 0; u < Cf::UT; ++u) {
             const int t = wave + W * u;
-            if (t < 3) copy16_to_lds((t == 0 ? p.cs : (t == 1 ? p.ct : p.dte)) + trow + lo, tdst + 256 * t);
-            else copy16_to_lds(p.cs + trow, junk);
+            if (t < 3) copy16_to_lds(((t == 0 ? p.cs : (t == 1 ? p.ct : p.dte)) + trow) + offt_h, tdst + 256 * t);
+            else if (W < 3) copy16_to_lds(p.cs + trow, junk);  // waves that copy several tables copy equally many
         }
     };
 
@@ -290,22 +335,38 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 
     const int nstep = (Qc + kStep - 1) / kStep;
     {
-        Frag<T> ba[2][KS], bb[2][KS];
-        load_b(0, ba);
-        issue_head(0, std::integral_constant<int, 0>{});
-        if (NBUF == 3 && hcnt > 1) issue_head(1, std::integral_constant<int, 1>{});
-        static_for<NBLK>([&](auto sc) __attribute__((always_inline)) {
-            constexpr int s = decltype(sc)::value;
-            if (s < nstep) {
-                auto step = [&](Frag<T> (&cur)[2][KS], Frag<T> (&nxt)[2][KS]) __attribute__((always_inline)) {
-                    if (s + 1 < nstep) load_b(s + 1, nxt);
-                    pair_a(std::integral_constant<int, 0>{}, sc, cur);
-                    if constexpr (MAXIT == 2) pair_a(std::integral_constant<int, 1>{}, sc, cur);
-                };
-                if constexpr (s % 2 == 0) step(ba, bb);
-                else step(bb, ba);
-            }
-        });
+        if constexpr (MAXIT == 2) {
+            // Two tiles: the wave visits (nearly) every step; B one step ahead.
+            Frag<T> ba[2][KS], bb[2][KS];
+            load_b(0, ba);
+            issue_head(0, std::integral_constant<int, 0>{});
+            if (NBUF == 3 && hcnt > 1) issue_head(1, std::integral_constant<int, 1>{});
+            static_for<NBLK>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int s = decltype(sc)::value;
+                if (s < nstep) {
+                    auto step = [&](Frag<T> (&cur)[2][KS], Frag<T> (&nxt)[2][KS]) __attribute__((always_inline)) {
+                        if (s + 1 < nstep) load_b(s + 1, nxt);
+                        pair_a(std::integral_constant<int, 0>{}, sc, cur);
+                        pair_a(std::integral_constant<int, 1>{}, sc, cur);
+                    };
+                    if constexpr (s % 2 == 0) step(ba, bb);
+                    else step(bb, ba);
+                }
+            });
+        } else {
+            // One tile: only the blocks up to its diagonal, one buffer (the
+            // other waves of the SIMD cover the load latency).
+            issue_head(0, std::integral_constant<int, 0>{});
+            if (NBUF == 3 && hcnt > 1) issue_head(1, std::integral_constant<int, 1>{});
+            static_for<NBLK>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int s = decltype(sc)::value;
+                if (s < nstep && s <= md[0] && live[0]) {
+                    Frag<T> bf[2][KS];
+                    load_b(s, bf);
+                    pair_a(std::integral_constant<int, 0>{}, sc, bf);
+                }
+            });
+        }
     }
 
     // Per-lane LDS offsets (elements).  Every swizzle depends only on the row
@@ -322,10 +383,6 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
 #pragma unroll
     for (int q = 0; q < PT; ++q)
         xoff[q] = rl * P + 8 * ((2 * q + ((il & 3) >> 1)) ^ xsw<WX>(rl)) + 4 * (il & 1);
-    //  - D x reads: row i = 16*t + il, columns 16*q + 4*grp .. +3.
-    int dxoff[PT];
-#pragma unroll
-    for (int q = 0; q < PT; ++q) dxoff[q] = il * P + 8 * ((2 * q + (grp >> 1)) ^ xsw<WX>(il)) + 4 * (grp & 1);
 
     // ---- phase B: heads; head hh lives in buffer hh % NBUF.
     T *yg = reinterpret_cast<T *>(p.y);
@@ -398,14 +455,32 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
             const bool use1 = MAXIT == 2 && live[MAXIT - 1] && m <= md[MAXIT - 1];
             if (!use0 && !use1) return;
             const T *xm = xsb + kStep * m * P;
-            Frag<T> xf[PT];
-#pragma unroll
-            for (int q = 0; q < PT; ++q) {
+            auto read_x = [&](int q) __attribute__((always_inline)) {
                 const i16x4 a0 = ds_read_tr16(xm + xoff[q]);
                 const i16x4 a1 = ds_read_tr16(xm + 16 * P + xoff[q]);
                 typedef short i16x8 __attribute__((ext_vector_type(8)));
-                xf[q].v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+                Frag<T> xq;
+                xq.v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+                return xq;
+            };
+            // Two tiles per wave: the block's x^T fragments are read once and
+            // serve both; one tile per wave: each is read just before its
+            // product (fewer live registers).
+            Frag<T> xf[MAXIT == 2 ? PT : 1];
+            if constexpr (MAXIT == 2) {
+#pragma unroll
+                for (int q = 0; q < PT; ++q) xf[q] = read_x(q);
             }
+            auto products = [&](auto kc, const Frag<T> &lf) __attribute__((always_inline)) {
+                constexpr int K = decltype(kc)::value;
+                if constexpr (MAXIT == 2) {
+#pragma unroll
+                    for (int q = 0; q < PT; ++q) mma(xf[q], lf, acc[K][q]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < PT; ++q) mma(read_x(q), lf, acc[K][q]);
+                }
+            };
             auto off_diag = [&](auto kc, const bf16x8 &gv) __attribute__((always_inline)) {
                 constexpr int K = decltype(kc)::value;
                 const float ai = exp2_hw(cs2i[K] - csv[kStep * m + kStep - 1] * kLog2e);
@@ -417,8 +492,7 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
                     lf.set(r, (float)gv[r] * (ai * d0[r]));
                     lf.set(4 + r, (float)gv[4 + r] * (ai * d1[r]));
                 }
-#pragma unroll
-                for (int q = 0; q < PT; ++q) mma(xf[q], lf, acc[K][q]);
+                products(kc, lf);
             };
             auto diag = [&](auto kc) __attribute__((always_inline)) {
                 constexpr int K = decltype(kc)::value;
@@ -435,8 +509,7 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
                     lf.set(r, (float)gd[K][r] * e0);
                     lf.set(4 + r, (float)gd[K][4 + r] * e1);
                 }
-#pragma unroll
-                for (int q = 0; q < PT; ++q) mma(xf[q], lf, acc[K][q]);
+                products(kc, lf);
             };
             if (use0) {
                 if constexpr (m < S0) {
@@ -460,7 +533,11 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
             }
         });
 
-        // + D x (x_i from the head's LDS rows), round to bf16, store.
+        // + D x (x_i from the head's LDS rows), round to bf16, store.  The
+        // row/column offsets are recomputed here from an opaque copy of the
+        // lane index (hoisted out of the head loop they would hold registers).
+        int ilo = il, grpo = grp;
+        asm volatile("" : "+v"(ilo), "+v"(grpo));
         if (late && ahead < hcnt) issue_head(ahead, std::integral_constant<int, (BI + NBUF - 1) % NBUF>{});
 
         // D through the constant address space: a scalar load, which vmcnt
@@ -471,8 +548,15 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
         // in issue order and loads complete in order (pending older stores
         // only make the wait stricter).
         if (NBUF == 3 && ahead < hcnt) {
-            if (has_prev) wait_vmcnt<NBUF == 3 ? Cf::UX + Cf::UH + Cf::UT : 0>();
-            else wait_vmcnt<NBUF == 3 ? Cf::UX + Cf::UT : 0>();
+            constexpr int CX = NBUF == 3 ? Cf::UX : 0, CH = NBUF == 3 ? Cf::UH : 0, CT = NBUF == 3 ? Cf::UT : 0;
+            const bool tab_wave = W < 3 || wave < 3;  // waves that copy the tables
+            if (has_prev) {
+                if (tab_wave) wait_vmcnt<CX + CH + CT>();
+                else wait_vmcnt<CX + CH>();
+            } else {
+                if (tab_wave) wait_vmcnt<CX + CT>();
+                else wait_vmcnt<CX>();
+            }
         } else {
             wait_vmcnt<0>();
         }
@@ -482,7 +566,9 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
             if (!live[k] || i >= Qc) continue;
 #pragma unroll
             for (int q = 0; q < PT; ++q) {
-                const V4 xv = *reinterpret_cast<const V4 *>(xsb + 16 * tile[k] * P + dxoff[q]);
+                // x_i[16q + 4grp .. +3]: row i = 16*t + il of the head's x buffer.
+                const int dxoff = ilo * P + 8 * ((2 * q + (grpo >> 1)) ^ xsw<WX>(ilo)) + 4 * (grpo & 1);
+                const V4 xv = *reinterpret_cast<const V4 *>(xsb + 16 * tile[k] * P + dxoff);
                 V4 out;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) out[r] = (T)(acc[k][q][r] + dh * (float)xv[r]);
@@ -501,9 +587,9 @@ __global__ __launch_bounds__(64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_he
     wait_vmcnt<0>();  // no copy outlives the workgroup
 }
 
-template <int NT, int PT, int NIT>
+template <int NT, int PT, int NIT, bool WIDE>
 hipError_t launch_nit(const Params &p, hipStream_t stream) {
-    using Cf = HeadsCfg<NT, PT, NIT>;
+    using Cf = HeadsCfg<NT, PT, NIT, WIDE>;
     if constexpr (Cf::LDS_BYTES > 160 * 1024) {
         return hipErrorNotSupported;
     } else {
@@ -513,21 +599,25 @@ hipError_t launch_nit(const Params &p, hipStream_t stream) {
         nslices = (p.heads_per_group + hps - 1) / hps;
         const int64_t total = base * nslices;
         const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-        hipLaunchKernelGGL((chunk_output_heads_kernel<NT, PT, NIT>), dim3((unsigned)(per_xcd * kXcds)),
+        hipLaunchKernelGGL((chunk_output_heads_kernel<NT, PT, NIT, WIDE>), dim3((unsigned)(per_xcd * kXcds)),
                            dim3(Cf::THREADS), 0, stream, p, hps, nslices);
         return hipGetLastError();
     }
 }
 
+// Shapes whose one-tile-per-wave variant fits 128 VGPRs.
+template <int NT, int PT>
+constexpr bool kWideOk = NT <= 8 && PT <= 4;
+
 template <int NT, int PT>
 hipError_t dispatch_q(const Params &p, hipStream_t stream) {
     switch (p.chunk) {
         case 8:
-        case 16: return launch_nit<NT, PT, 1>(p, stream);
-        case 32: return launch_nit<NT, PT, 2>(p, stream);
-        case 64: return launch_nit<NT, PT, 4>(p, stream);
-        case 128: return launch_nit<NT, PT, 8>(p, stream);
-        case 256: return launch_nit<NT, PT, 16>(p, stream);
+        case 16: return launch_nit<NT, PT, 1, false>(p, stream);
+        case 32: return launch_nit<NT, PT, 2, false>(p, stream);
+        case 64: return launch_nit<NT, PT, 4, false>(p, stream);
+        case 128: return launch_nit<NT, PT, 8, kWideOk<NT, PT>>(p, stream);
+        case 256: return launch_nit<NT, PT, 16, kWideOk<NT, PT>>(p, stream);
         default: return hipErrorNotSupported;
     }
 }
