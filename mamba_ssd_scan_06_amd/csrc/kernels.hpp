@@ -38,6 +38,9 @@ struct Params {
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
 hipError_t launch_chunk_cumsum(const Params &p, hipStream_t stream);
 hipError_t launch_chunk_state(const Params &p, Elem e, hipStream_t stream);
+// Head-batched bf16 chunk states; returns hipErrorNotSupported when the shape
+// does not fit its LDS budget or wave split (the caller then uses launch_chunk_state).
+hipError_t launch_chunk_state_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_pass(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // Head-batched bf16 chunk outputs; returns hipErrorNotSupported when the

@@ -247,7 +247,13 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
         run.step("empty_sequence", [&] { return ssd::launch_empty_sequence(p, stream); });
     } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
-        run.step("chunk_state", [&] { return ssd::launch_chunk_state(p, e, stream); });
+        run.step("chunk_state", [&] {
+            if (e == ssd::Elem::BF16) {
+                const hipError_t r = ssd::launch_chunk_state_heads(p, stream);
+                if (r != hipErrorNotSupported) return r;
+            }
+            return ssd::launch_chunk_state(p, e, stream);
+        });
         run.step("state_pass", [&] { return ssd::launch_state_pass(p, e, stream); });
         run.step("chunk_output", [&] {
             if (e == ssd::Elem::BF16) {
