@@ -91,6 +91,13 @@ def algorithmic_work(wl, idx=None):
             flops=b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P for q in qs)
             + 2 * b * H * N * P * sum(q for c, q in enumerate(qs) if c > 0 or wl.init_state)),
     }
+    if 1 <= T <= 32 and nc == 1:
+        # one fused kernel: h0 read once, both states written once
+        toks = [min(j, T - 1) + 1 if j >= 0 else 0 for j in (idx if idx is not None else [])] if wl.state_out else []
+        work["one_chunk"] = dict(
+            bytes=2 * x + 2 * bc + dt + (st if wl.init_state else 0) + st + (st if wl.state_out else 0),
+            flops=b * (G * T * (T + 1) * N + H * T * (T + 1) * P) + 4 * b * H * P * N * T
+            + 2 * H * P * N * sum(toks))
     if wl.state_out:
         Q = wl.chunk
         toks = [(j % Q) + 1 if j >= 0 else 0 for j in (idx if idx is not None else [])]

@@ -90,7 +90,8 @@ typedef struct {
 
 /* Where the intermediates live inside the workspace after a call (byte
  * offsets from the workspace pointer).  Exposed so that the individual steps
- * can be checked:
+ * can be checked.  A call whose tokens fit one chunk and number at most 32
+ * is computed by one fused kernel and leaves the workspace untouched.
  *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
  *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
  *            past seqlen count as dt = 0.

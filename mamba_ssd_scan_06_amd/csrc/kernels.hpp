@@ -47,6 +47,10 @@ hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // shape does not fit its LDS budget (the caller then uses launch_chunk_output).
 hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_at_index(const Params &p, Elem e, hipStream_t stream);
+// Whole forward of a one-chunk call of at most 32 tokens in one kernel (y,
+// final_state, state_out; the workspace is not used).  Returns
+// hipErrorNotSupported for other calls and unsupported shapes.
+hipError_t launch_one_chunk(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_empty_sequence(const Params &p, hipStream_t stream);
 
 }  // namespace ssd

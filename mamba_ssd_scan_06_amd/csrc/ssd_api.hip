@@ -9,6 +9,9 @@
 //   3. state_pass       states, cs, h0   -> prev[c] = h_{c-1}, hj, final_state (yellow)
 //   4. chunk_output     x, B, C, cs, dt tables, prev, D -> y  (orange + blue + D skip)
 //   5. state_at_index   x, B, cs, dt, hj -> state_out  (only with state_out)
+// A call whose tokens fit one chunk of at most 32 tokens (the multi-step
+// verify) instead runs one fused kernel, one_chunk, which writes y,
+// final_state and state_out directly and leaves the workspace untouched.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -113,10 +116,9 @@ struct Launcher {
     const char *failed_step = "";
     int count = 0;
 
-    template <typename F>
-    void step(const char *name, F &&launch) {
-        if (err != hipSuccess) return;
-        err = launch();
+    // Records the outcome of one launch and the caller's mark after it.
+    void record(const char *name, hipError_t r) {
+        err = r;
         if (err != hipSuccess) {
             failed_step = name;
             return;
@@ -127,6 +129,24 @@ struct Launcher {
             if (err != hipSuccess) failed_step = "event record";
             if (names) names[count - 1] = name;
         }
+    }
+
+    template <typename F>
+    void step(const char *name, F &&launch) {
+        if (err != hipSuccess) return;
+        record(name, launch());
+    }
+
+    // Like step, but a launcher answering hipErrorNotSupported (a call or
+    // shape it does not take, nothing enqueued) leaves no trace and makes
+    // it return false.
+    template <typename F>
+    bool try_step(const char *name, F &&launch) {
+        if (err != hipSuccess) return true;
+        const hipError_t r = launch();
+        if (r == hipErrorNotSupported) return false;
+        record(name, r);
+        return true;
     }
 };
 
@@ -245,6 +265,8 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     if (n_marks > 0) run.err = hipEventRecord(static_cast<hipEvent_t>(marks[0]), stream);
     if (T == 0) {
         run.step("empty_sequence", [&] { return ssd::launch_empty_sequence(p, stream); });
+    } else if (run.try_step("one_chunk", [&] { return ssd::launch_one_chunk(p, e, stream); })) {
+        // short call: the whole forward in one kernel
     } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
         run.step("chunk_state", [&] {

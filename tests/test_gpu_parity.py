@@ -243,6 +243,32 @@ def test_edge_shapes(case):
         check(k, got[k], ref[k], TOL[dtype])
 
 
+# Calls that fit one chunk of at most 32 tokens take the fused one-kernel
+# path (the multi-step verify); the shapes below cover T = 1, T < Q, T = Q =
+# 32, N = 256, fp32, no initial state and no D.
+ONE_CHUNK = [
+    # b, T, H, P, N, G, Q, dtype, init_state
+    (2, 1, 4, 64, 128, 1, 8, "bf16", True),
+    (3, 5, 6, 128, 64, 3, 8, "bf16", True),
+    (2, 32, 4, 64, 256, 2, 32, "bf16", True),
+    (2, 31, 2, 32, 64, 1, 64, "f32", True),
+    (2, 8, 4, 128, 128, 4, 16, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", ONE_CHUNK, ids=lambda c: "b{}_T{}_H{}_P{}_N{}_G{}_Q{}_{}_init{}".format(*c))
+def test_one_chunk_fused(case):
+    b, T, H, P, N, G, Q, dtype, init = case
+    wl = workload("one_chunk", b, T, H, P, N, G, Q, dtype, init_state=init, state_out=True, seed=131 + T)
+    announce(f"one chunk {wl}")
+    inp = ssd_inputs.generate(wl)
+    got, ref = gpu_run(inp), oracle_run(inp)
+    for k in ("y", "final", "state_out"):
+        check(k, got[k], ref[k], TOL[dtype])
+    got0, ref0 = gpu_run(inp, use_D=False), oracle_run(inp, use_D=False)
+    check("y without D", got0["y"], ref0["y"], TOL[dtype])
+
+
 def test_empty_sequence():
     announce("empty sequence T=0")
     h0 = torch.randn(2, 4, 64, 128, device="cuda")
