@@ -86,8 +86,13 @@ struct HeadsCfg {
     static constexpr int UX = (IXH + W - 1) / W;                // copies per wave per head: x
     static constexpr int UH = (IHH + W - 1) / W;                //   initial state
     static constexpr int UT = (3 + W - 1) / W;                  //   tables
+    // Phase A of the one-tile layout streams B through a ring of RING
+    // 32-token slots (IB 1 KB copies per slot).
+    static constexpr int RSLOT = kStep * NP, RING = 4;
+    static constexpr int IB = kStep * WB / 64;
+    static constexpr int IB_W = (IB + W - 1) / W;
     static constexpr size_t lds_bytes(int nbuf) {
-        return (size_t)nbuf * ((XE + HE) * 2 + 3 * 256 * 4) + 512 * 2;
+        return (size_t)nbuf * ((XE + HE) * 2 + 3 * 256 * 4) + 512 * 2 + (WIDE ? (size_t)RING * RSLOT * 2 : 0);
     }
     // Head buffers: three (copies run two heads ahead) when they fit in LDS
     // and one head's copies per wave fit the vmcnt counter.
@@ -129,6 +134,16 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
     __shared__ __align__(16) T hb0[HE], hb1[HE], hb2[NBUF == 3 ? HE : 8];
     __shared__ __align__(16) float tb0[3 * 256], tb1[3 * 256], tb2[NBUF == 3 ? 3 * 256 : 4];  // cs, ct, dte
     __shared__ __align__(16) T junk[512];  // target of padding copies (never read)
+    // B ring of phase A (one-tile layout), one LDS object per slot.
+    __shared__ __align__(16) T rg0[WIDE ? Cf::RSLOT : 8], rg1[WIDE ? Cf::RSLOT : 8], rg2[WIDE ? Cf::RSLOT : 8],
+        rg3[WIDE ? Cf::RSLOT : 8];
+    auto ring = [&](auto sc) __attribute__((always_inline)) -> T * {
+        constexpr int k = decltype(sc)::value % Cf::RING;
+        if constexpr (k == 0) return rg0;
+        else if constexpr (k == 1) return rg1;
+        else if constexpr (k == 2) return rg2;
+        else return rg3;
+    };
     auto xbuf = [&](auto bc) __attribute__((always_inline)) -> T * {
         if constexpr (decltype(bc)::value == 0) return xb0;
         else if constexpr (decltype(bc)::value == 1) return xb1;
@@ -275,6 +290,12 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
         }
     };
 
+    // 16-byte-per-lane reads of h and of the B ring: row 16*a + il, piece
+    // 4*ks + grp (swizzle period 16, so a per-lane constant).
+    int roff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = il * NP + 8 * ((4 * ks + grp) ^ swz_rows16<WB>(il));
+
     // ---- phase A: causal tiles of G^T = B C^T.  B fragments come straight
     // from global memory (each 32-token step of B is read by every wave, from
     // L2 after the first), one step ahead of the products.
@@ -353,17 +374,63 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
                     else step(bb, ba);
                 }
             });
-        } else {
-            // One tile: only the blocks up to its diagonal, one buffer (the
-            // other waves of the SIMD cover the load latency).
+        } else if constexpr (!WIDE) {
+            // One tile of at most 16 tokens (one j block): B from global memory.
             issue_head(0, std::integral_constant<int, 0>{});
             if (NBUF == 3 && hcnt > 1) issue_head(1, std::integral_constant<int, 1>{});
+            if (live[0]) {
+                Frag<T> bf[2][KS];
+                load_b(0, bf);
+                pair_a(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, bf);
+            }
+        } else {
+            // One tile: B streams through the LDS ring, RING-1 steps ahead;
+            // each wave multiplies only the blocks up to its diagonal.  Every
+            // wave issues IB_W copies per step (padding copies go to junk),
+            // so one count waits for a step.
+            const T *bsrc = bg + ((b * L + t0) * G + g) * N;
+            auto issue_b = [&](int step, auto slot) __attribute__((always_inline)) {
+                T *dst = ring(slot);
+#pragma unroll
+                for (int u = 0; u < Cf::IB_W; ++u) {
+                    const int ins = wave + W * u;
+                    if (ins < Cf::IB) {
+                        const int U = 64 * ins + lane;
+                        const int row = U / WB, pos = U - row * WB;
+                        int gc = pos ^ swz_rows16<WB>(row);
+                        if constexpr (NP != N) gc %= N / 8;
+                        const int j = min(kStep * step + row, Qc - 1);
+                        copy16_to_lds(bsrc + (int64_t)j * G * N + 8 * gc, dst + ins * 512);
+                    } else {
+                        copy16_to_lds(bsrc, junk);
+                    }
+                }
+            };
+            issue_head(0, std::integral_constant<int, 0>{});
+            static_for<Cf::RING - 1>([&](auto sc) __attribute__((always_inline)) {
+                if (decltype(sc)::value < nstep) issue_b(decltype(sc)::value, sc);
+            });
             static_for<NBLK>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int s = decltype(sc)::value;
-                if (s < nstep && s <= md[0] && live[0]) {
-                    Frag<T> bf[2][KS];
-                    load_b(s, bf);
-                    pair_a(std::integral_constant<int, 0>{}, sc, bf);
+                if (s < nstep) {
+                    // Step s has landed once at most RING-2 later steps are pending.
+                    if (s + Cf::RING - 2 < nstep) wait_vmcnt<Cf::IB_W * (Cf::RING - 2)>();
+                    else wait_vmcnt<0>();
+                    // ... for every wave; and slot (s-1) % RING is no longer read (its
+                    // reads feed products that need not be issued yet, hence
+                    // the LDS wait before the barrier).
+                    lds_barrier();
+                    if (s + Cf::RING - 1 < nstep)
+                        issue_b(s + Cf::RING - 1, std::integral_constant<int, s + Cf::RING - 1>{});
+                    if (s <= md[0] && live[0]) {
+                        const T *rb = ring(sc);
+                        Frag<T> bf[2][KS];
+#pragma unroll
+                        for (int half = 0; half < 2; ++half)
+#pragma unroll
+                            for (int ks = 0; ks < KS; ++ks) load8(bf[half][ks], rb + 16 * half * NP + roff[ks]);
+                        pair_a(std::integral_constant<int, 0>{}, sc, bf);
+                    }
                 }
             });
         }
@@ -372,10 +439,6 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
     // Per-lane LDS offsets (elements).  Every swizzle depends only on the row
     // modulo a period dividing 16, so a fragment's address is a per-lane
     // constant plus a wave-uniform row offset.
-    //  - 16-byte-per-lane reads of h: row 16*a + il, piece 4*ks + grp.
-    int roff[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) roff[ks] = il * NP + 8 * ((4 * ks + grp) ^ swz_rows16<WB>(il));
     //  - transposing reads of x: source lane (il = 4*kr + a) points at row
     //    16*half + 4*grp + kr, columns 16*q + 4*a .. +3.
     const int rl = 4 * grp + (il >> 2);
