@@ -255,6 +255,39 @@ def traffic_from_profile(kernel, workload):
         return None
 
 
+# Single-token decode at the 2.7B-layer shape: the state updated in place.
+DECODE = ssd_inputs.Workload("decode_2.7b_b256", 256, 1, 80, 64, 128, 1, 256, "bf16", init_state=True, seed=1101)
+
+
+def time_decode(steps, warmup, device):
+    """One-token calls with final_state = init_state (in place), back to back."""
+    import torch
+
+    import mamba_ssd_scan_06_amd as ssd
+
+    wl = DECODE
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp, device)
+    h = dev["init_state"]
+    y = torch.empty_like(dev["x"])
+    args = (dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], h, wl.chunk)
+    for _ in range(warmup):
+        ssd.ssd_chunk_scan_fwd(*args, y=y, final_state=h)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        ssd.ssd_chunk_scan_fwd(*args, y=y, final_state=h)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    b, H, P, N = wl.batch, wl.nheads, wl.headdim, wl.dstate
+    state_bytes = 2 * b * H * P * N * 4  # read and write the fp32 state
+    return {"workload": wl.name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "in_place": True,
+            "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "state_GB/s": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(wl, inp):
     import oracle
 
@@ -424,6 +457,7 @@ def main():
                                "kernel_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
             del inp2
 
+    decode = None if args.headline_only else time_decode(max(20, args.steps // 2), 5, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, inp)
     line = {
         "metric": METRIC,
@@ -448,6 +482,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "workloads": workloads,
+        "decode": decode,
         "input_sha256": inp.sha256,
     }
     if args.copy_probe:

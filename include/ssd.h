@@ -148,7 +148,9 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
  *                 16-byte aligned; contents on entry are ignored
  *   hip_stream    hipStream_t as void*, NULL for the default stream
  *
- * Outputs must not overlap inputs, each other or the workspace.
+ * Outputs must not overlap inputs, each other or the workspace, with one
+ * exception: final_state may be init_state itself (same pointer), updating
+ * the state in place (a decode step, a verifier keeping its cache).
  * Errors: see ssd_status; checks are host-side and happen before any launch. */
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const void *B, const void *C, const float *D,

@@ -79,9 +79,9 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(Params p, bool at_inde
     if (at_index) {
         int j = p.state_out_idx[b];
         j = j < -1 ? -1 : (j > L - 1 ? (int)(L - 1) : j);
-        if (j < 0) {  // nothing accepted: the state is the initial one
+        if (j < 0) {  // nothing accepted: the state is the initial one, kept in hj by the state pass
             float *dst = p.state_out + (b * H + h) * (int64_t)P * N;
-            const float *src = p.init_state ? p.init_state + (b * H + h) * (int64_t)P * N : nullptr;
+            const float *src = p.hj + (b * H + h) * (int64_t)P * N;
             for (int e = tid * 4; e < P * N; e += 256 * 4)
                 *reinterpret_cast<f32x4 *>(dst + e) =
                     src ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{0.f, 0.f, 0.f, 0.f};

@@ -220,9 +220,15 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
                             range("init_state", init_state, state_bytes),
                             range("state_out_idx", state_out_idx, b * sizeof(int32_t)),
                             range("workspace", workspace, L.total)};
+    // final_state may be init_state itself (an in-place update, e.g. decode):
+    // every kernel reads each initial-state element before that element is
+    // written, in the same thread, and reads it nowhere else.
+    const bool in_place = final_state != nullptr && (const void *)final_state == (const void *)init_state;
     for (int i = 0; i < 3; ++i) {
-        for (const Range &o : others)
+        for (const Range &o : others) {
+            if (in_place && i == 1 && o.lo == (uintptr_t)init_state) continue;
             if (overlaps(outs[i], o)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, o.name);
+        }
         for (int k = i + 1; k < 3; ++k)
             if (overlaps(outs[i], outs[k])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[k].name);
     }

@@ -13,7 +13,8 @@
 //             only when there is an initial state (otherwise it is zero and
 //             never read);
 //   hj      = h_{c_j-1} in fp32 for c_j = the chunk of state_out_idx[b], when
-//             the state at that index is requested;
+//             the state at that index is requested (the initial state when
+//             that index is -1);
 //   final_state = h_{nc-1}.
 // The chunk states themselves are left as they are.
 //
@@ -59,11 +60,14 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
     const int64_t stride = (int64_t)H * pn4;           // one chunk further
     const f32x4 *st = reinterpret_cast<const f32x4 *>(p.states) + first;
     T *prev = reinterpret_cast<T *>(p.prev) + 4 * first;
-    int cj = -1;  // chunk whose entering state the state-at-index step reads
+    int cj = -2;  // chunk whose entering state the state-at-index step reads
     if (p.hj && p.state_out_idx) {
         const int j = p.state_out_idx[b];
         cj = j < 0 ? -1 : (int)(min((int64_t)j, p.seqlen - 1) / Q);
     }
+    // Nothing accepted: the state-at-index step copies the initial state
+    // from hj (init_state itself may be overwritten by final_state).
+    if (cj == -1) reinterpret_cast<f32x4 *>(p.hj)[e] = hc;
 
 #pragma unroll 1
     for (int c0 = 0; c0 < nc; c0 += kBatchChunks) {

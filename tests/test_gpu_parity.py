@@ -269,6 +269,48 @@ def test_one_chunk_fused(case):
     check("y without D", got0["y"], ref0["y"], TOL[dtype])
 
 
+def test_decode_in_place():
+    # Three single-token steps that update the state in place (final_state is
+    # init_state) equal one call over the three tokens.
+    wl = workload("decode", 16, 3, 8, 64, 128, 2, 64, "bf16", init_state=True, seed=141)
+    announce(f"decode in place {wl}")
+    inp = ssd_inputs.generate(wl)
+    ref = oracle_run(inp)
+    dev = device_inputs(inp)
+    h = dev["init_state"].clone()
+    ys = []
+    for t in range(wl.seqlen):
+        sl = slice(t, t + 1)
+        y, fin, _ = ssd.ssd_chunk_scan_fwd(dev["x"][:, sl].contiguous(), dev["dt"][:, sl].contiguous(), dev["A"],
+                                           dev["B"][:, sl].contiguous(), dev["C"][:, sl].contiguous(), dev["D"],
+                                           h, 64, final_state=h)
+        assert fin.data_ptr() == h.data_ptr()
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_all = torch.cat(ys, dim=1).float().cpu().numpy()
+    check("y", y_all, ref["y"], 2e-2)
+    check("state", h.cpu().numpy(), ref["final"], 2e-2)
+
+
+@pytest.mark.parametrize("T", [300, 20])
+def test_in_place_with_state_out(T):
+    # final_state == init_state on the chunked path (T = 300) and the fused
+    # one-chunk path (T = 20), with accepted indices including -1.
+    wl = workload("inplace", 4, T, 4, 64, 64, 2, 64, "bf16", init_state=True, state_out=True, seed=151 + T)
+    announce(f"in place {wl}")
+    inp = ssd_inputs.generate(wl)
+    idx = np.array([-1, 0, T // 2, T - 1], np.int32)
+    ref = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state, idx)
+    dev = device_inputs(inp)
+    h = dev["init_state"].clone()
+    y, fin, sout = ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], h, 64,
+                                          torch.from_numpy(idx).cuda(), final_state=h)
+    torch.cuda.synchronize()
+    check("y", y.float().cpu().numpy(), ref[0], 2e-2)
+    check("final (in place)", h.cpu().numpy(), ref[1], 2e-2)
+    check("state_out", sout.cpu().numpy(), ref[2], 2e-2)
+
+
 def test_empty_sequence():
     announce("empty sequence T=0")
     h0 = torch.randn(2, 4, 64, 128, device="cuda")
