@@ -33,6 +33,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,7 +49,7 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and MFMA)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
-    "chunk_state": ["chunk_state.hip", "device_common.hpp"],
+    "chunk_state": ["chunk_state_heads.hip", "chunk_state.hip", "device_common.hpp"],
     "state_pass": ["state_pass.hip", "device_common.hpp"],
     "chunk_output": ["chunk_output_heads.hip", "chunk_output.hip", "device_common.hpp"],
     "state_at_index": ["chunk_state.hip", "device_common.hpp"],
@@ -356,9 +357,10 @@ def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
     copy_bytes = 256 << 20
 
     def find(d, key):
-        # kernel symbols look like "...chunk_output_heads_kernel<8, 4, 16>(...)"; the
+        # kernel symbols look like "...chunk_output_heads_kernel<8, 4, 16, true>(...)"; the
         # step's kernel is the matching one with the most dispatches
-        hits = {k: v for k, v in d.items() if key in k}
+        pat = re.compile(rf"(?<![a-z_]){re.escape(key)}(_heads|_dma)?_kernel") if key != "copy" else None
+        hits = {k: v for k, v in d.items() if (pat.search(k) if pat else key in k)}
         return max(hits.items(), key=lambda kv: len(kv[1])) if hits else (None, None)
 
     _, cf = find(fetch, "copy")

@@ -73,6 +73,21 @@ def gpu_run(inp, chunk=None, use_D=True, use_init=True, use_state_out=True, dev=
     return out
 
 
+def kernel_names(inp, chunk=None, dev=None):
+    """Names of the kernels one call launches (through the marked entry point)."""
+    dev = dev or device_inputs(inp)
+    chunk = chunk or inp.wl.chunk
+    evs = [torch.cuda.Event() for _ in range(8)]
+    for e in evs:
+        e.record()  # creates the event
+    torch.cuda.synchronize()
+    *_, names = ssd.ssd_chunk_scan_fwd_marked(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"],
+                                              dev["init_state"], chunk, dev["state_out_idx"],
+                                              marks=[e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    return names
+
+
 def oracle_run(inp, use_D=True, use_init=True, use_state_out=True, chunk=0):
     y, fin, sout, cst = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D if use_D else None,
                                            inp.init_state if use_init else None,
