@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "chunk_state": ["chunk_state_heads.hip", "chunk_state.hip", "device_common.hpp"],
     "state_pass": ["state_pass.hip", "device_common.hpp"],
     "chunk_output": ["chunk_output_heads.hip", "chunk_output.hip", "device_common.hpp"],
+    "chunk_scan_fused": ["chunk_scan_fused.hip", "device_common.hpp"],
     "state_at_index": ["chunk_state.hip", "device_common.hpp"],
 }
 CSRC = os.path.join(ROOT, "mamba_ssd_scan_06_amd", "csrc")
@@ -92,6 +93,10 @@ def algorithmic_work(wl, idx=None):
             flops=b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P for q in qs)
             + 2 * b * H * N * P * sum(q for c, q in enumerate(qs) if c > 0 or wl.init_state)),
     }
+    # single pass: x, B, C and the tables read once, y and the states written once
+    work["chunk_scan_fused"] = dict(
+        bytes=2 * x + 2 * bc + 3 * tab + (st if wl.init_state else 0) + st + (st if wl.state_out else 0),
+        flops=work["chunk_state"]["flops"] + work["chunk_output"]["flops"])
     if 1 <= T <= 32 and nc == 1:
         # one fused kernel: h0 read once, both states written once
         toks = [min(j, T - 1) + 1 if j >= 0 else 0 for j in (idx if idx is not None else [])] if wl.state_out else []
@@ -371,7 +376,7 @@ def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
     w_copy = copy_bytes / (sorted(cw)[len(cw) // 2] * 1024.0)
     wl = ssd_inputs.WORKLOADS[workload]
     work = algorithmic_work(wl)
-    for kernel in ("chunk_output", "chunk_state", "state_pass", "chunk_cumsum"):
+    for kernel in ("chunk_scan_fused", "chunk_output", "chunk_state", "state_pass", "chunk_cumsum"):
         kf_name, kf = find(fetch, kernel)
         _, kw = find(write, kernel)
         if not kf or not kw:

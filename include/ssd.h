@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -99,6 +99,11 @@ typedef struct {
  *            so that dt_j exp(cs_i - cs_j) = exp2(cs_i log2(e) - ct_j).
  *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
  *            (within seqlen) of the 32-token block holding i.
+ *   block_decay fp32 [batch, nheads, nchunks, 16]: for the chunk's 32-token
+ *            blocks m = 0..7, entry m is cs * log2(e) at the block's last
+ *            token e(m) and entry 8+m is exp(cs_e(m) - cs_e(m-1))
+ *            (exp(cs_e(0)) for m = 0); blocks past the chunk repeat its
+ *            last token.
  *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: entry c is the
  *            state chunk c reaches from a zero initial state.
  *   prev     dtype, same layout: entry c is the state entering chunk c,
@@ -110,6 +115,7 @@ typedef struct {
     size_t cumsum_offset;
     size_t ct_offset;
     size_t dt_decay_offset;
+    size_t block_decay_offset;
     size_t states_offset;
     size_t prev_offset;
     size_t hj_offset;

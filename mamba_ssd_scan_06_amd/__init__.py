@@ -37,7 +37,8 @@ class ssd_shape(ctypes.Structure):
 
 class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("cumsum_offset", ctypes.c_size_t), ("ct_offset", ctypes.c_size_t),
-                ("dt_decay_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
+                ("dt_decay_offset", ctypes.c_size_t), ("block_decay_offset", ctypes.c_size_t),
+                ("states_offset", ctypes.c_size_t),
                 ("prev_offset", ctypes.c_size_t), ("hj_offset", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t),
                 ("nchunks", ctypes.c_int64)]

@@ -31,6 +31,8 @@ namespace {
 
 constexpr int kHeads = 4;   // heads (waves) per workgroup
 constexpr int kBlock = 32;  // token block of dte
+constexpr int kBlk = 8;     // blocks per chunk in the block-factor table (chunks of at most 256 tokens)
+static_assert(2 * kBlk <= kBlkStride, "block-factor row");
 constexpr double kLog2eD = 1.4426950408889634074;
 
 __device__ inline double shfl_up_f64(double v, int delta, int lane) {
@@ -119,6 +121,28 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
             csv[v] = cs_i;
             ctv[v] = ct;
             dtev[v] = de;
+        }
+    }
+    // Per 32-token block m: cs*log2(e) at the block's last token e(m)
+    // (clipped to the chunk's last valid token) and the decay between block
+    // ends, exp(cs_e(m) - cs_e(m-1)) (exp(cs_e(0)) for m = 0), both from the
+    // fp64 sums with one rounding.
+    if (p.blk) {
+        const int m = lane;                  // one block per lane
+        const int e = min(kBlock * m + kBlock - 1, max(Qc - 1, 0));
+        double sm = 0.0, sp = 0.0;           // sums at e(m) and e(m-1)
+        const int ep = m > 0 ? min(kBlock * m - 1, max(Qc - 1, 0)) : -1;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const double o = shfl_f64(s[v], e / VPT);
+            if (e % VPT == v) sm = o;
+            const double op = shfl_f64(s[v], max(ep, 0) / VPT);
+            if (ep >= 0 && ep % VPT == v) sp = op;
+        }
+        if (m < kBlk) {
+            float *row = p.blk + ((b * H + h) * nc + c) * (int64_t)kBlkStride;
+            row[m] = (float)(a * sm * kLog2eD);
+            row[kBlk + m] = exp_neg((float)(a * (sm - sp)));
         }
     }
     if (i0 < Q) {

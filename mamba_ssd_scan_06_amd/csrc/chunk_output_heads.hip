@@ -102,21 +102,6 @@ struct HeadsCfg {
     static constexpr size_t LDS_BYTES = lds_bytes(NBUF);
 };
 
-// Tile of wave w in the one-tile-per-wave layout.  Waves w, w+4, w+8, w+12
-// share a SIMD; tile t meets t/2 + 1 causal blocks, and these orders give
-// every SIMD the same number.
-template <int NIT>
-__device__ __forceinline__ int wide_tile(int w) {
-    if constexpr (NIT == 16) {
-        constexpr unsigned long long map = 0xdcfeab894567'3210ull;  // nibble w = tile of wave w
-        return (int)((map >> (4 * w)) & 15);
-    } else if constexpr (NIT == 8) {
-        return w < 4 ? w : 11 - w;
-    } else {
-        return w;
-    }
-}
-
 template <int NT, int PT, int NIT, bool WIDE>
 __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_heads_kernel(Params p, int hps,
                                                                                                   int nslices) {

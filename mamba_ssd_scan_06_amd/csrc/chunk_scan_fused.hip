@@ -1,0 +1,504 @@
+// Single-pass SSD forward (bf16): one workgroup per (sequence b, head h)
+// walks the chunks in order and keeps the running state in registers, so all
+// four parts of the block decomposition of "Transformers are SSMs"
+// (cloud.tencent.com.cn, section "SSD算法") run in one kernel: the chunk
+// states and the states entering each chunk never reach memory, x is read
+// once and y written once.  The state passing is the sequential scan over
+// chunks that section "深入解析分块与状态传递机制" describes, here carried
+// by the workgroup itself.
+//
+// Chunk c (tokens t0 .. t0+Qc-1, head h of group g), with cs the chunk-local
+// cumulative log-decay, cs2 = cs log2(e), ct = cs2 - log2(dt), e(m) the last
+// token of 32-token block m and dte_j = dt_j exp(cs_e(m) - cs_j) for j in m
+// (the tables of the cumsum kernel, which also gives cs2_e(m) and the
+// state's Horner factors per block):
+//   G      = C_c B_c^T (causal 16x32 tiles, bf16, nearest even)
+//   orange y_i  = sum_{j<=i} exp(cs_i - cs_j) dt_j G_ij x_j
+//   blue   y_i += exp(cs_i) C_i . h_{c-1}
+//   green  h_c  = exp(cs_last) h_{c-1} + sum_j exp(cs_last - cs_j) dt_j x_j B_j^T
+//          y_i += D_h x_i.
+// Decay factors.  Outside the diagonal blocks every factor splits into the
+// per-token dte_j, applied once to x (xd = dte x, rounded to bf16), and
+// factors of at most 1 that depend on the block only:
+//   orange, block m < md (md the tile's diagonal block): G_ij times
+//     exp2(cs2_i - cs2_e(m)), rounded to bf16, on xd;
+//   blue: exp2(cs2_i) times C_i . h_{c-1};
+//   state, in Horner form: acc = h_{c-1}; acc = acc g_m + B_m^T xd_m over the
+//     chunk's blocks, g_0 = exp2(cs2_e(0)), g_m = exp2(cs2_e(m) - cs2_e(m-1)),
+//     which leaves h_c (e of the last block is the chunk's last token).
+// The diagonal block keeps the exact factor exp2(cs2_i - ct_j) per element
+// on raw x (the mask applied through the exponent), so it stays exact
+// however strong the decay inside a block; the skip term D x_i enters as D
+// added to its j = i coefficient before rounding.
+//
+// Work split: NIT = Q/16 waves, each owning one 16-row tile (balanced so
+// that every SIMD meets the same number of causal blocks) and, for the
+// state, NTW x PTW of its 16x16 tiles.  LDS holds the chunk's B rows, x and
+// xd rows (token-major, read with the transposing LDS read) and h_{c-1} in
+// bf16.  While chunk c computes, chunk c+1's x and B rows are loaded into
+// registers and its tables copied to LDS; its C rows follow once chunk c no
+// longer needs them.  At the switch every wave waits for its loads and
+// writes the next chunk's LDS, and one barrier publishes them.  y is stored
+// before the state part, whose products cover the stores' latency.  Global
+// accesses go through buffer descriptors over each chunk's rows, with fixed
+// per-lane offsets.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kStep = 32;  // tokens per j block
+
+template <int NT, int PT, int NIT>
+struct FusedCfg {
+    static constexpr int N = NT * 16, P = PT * 16, Q = NIT * 16;
+    static constexpr int W = NIT, THREADS = 64 * NIT;          // one 16-row tile per wave
+    static constexpr int KS = N / 32;                            // 32-wide k steps over n
+    static constexpr int WB = N / 8, WX = P / 8;                 // 16-byte pieces per B row, per x row
+    static constexpr int NBLK = Q / kStep;
+    static constexpr int WPN = NT < W ? NT : W, WPP = W / WPN;  // waves along n, p (state tiles)
+    static constexpr int NTW = NT / WPN, PTW = PT / WPP;         // state tiles per wave
+    static constexpr int UXR = Q * WX / THREADS;                 // 16-byte x pieces per thread
+    static constexpr int UBR = Q * WB / THREADS;                 // 16-byte B pieces per thread
+    static constexpr size_t LDS_BYTES =
+        (size_t)Q * N * 2 + 2 * (size_t)Q * P * 2 + (size_t)P * N * 2 + 2 * 3 * 256 * 4;
+    static constexpr bool OK = NIT >= 8 && NT >= 2 && NT % WPN == 0 && PT % WPP == 0 && PTW >= 1 &&
+                               (Q * WX) % THREADS == 0 && UXR >= 1 && (Q * WB) % THREADS == 0 &&
+                               LDS_BYTES <= 160 * 1024;
+};
+
+// Raw buffer descriptor over [base, base + bytes): loads beyond it read 0
+// and stores beyond it are dropped, which takes care of rows past the end of
+// the sequence.  Word 3 selects 32-bit data, the gfx9 value for untyped access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int NT, int PT, int NIT>
+__global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
+    using Cf = FusedCfg<NT, PT, NIT>;
+    using T = bf16;
+    constexpr int N = Cf::N, P = Cf::P, Q = Cf::Q, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
+    constexpr int NBLK = Cf::NBLK, NTW = Cf::NTW, PTW = Cf::PTW, UXR = Cf::UXR, UBR = Cf::UBR;
+    constexpr int THREADS = Cf::THREADS;
+    constexpr int RX = THREADS / WX, RB = THREADS / WB;  // rows between a thread's x / B pieces
+    static_assert(RX % 8 == 0 && RB % 8 == 0, "a thread's pieces share one swizzle");
+    typedef typename Vec8<T>::type V8;
+    typedef typename Vec4<T>::type V4;
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+    __shared__ __align__(16) T bl[Q * N];   // B rows, pieces swizzled for the transposing read
+    __shared__ __align__(16) T xs[Q * P];   // x rows
+    __shared__ __align__(16) T xd[Q * P];   // dte * x rows
+    __shared__ __align__(16) T hb[P * N];   // h_{c-1} rows p, pieces swizzled for 16-byte reads
+    // cs, ct, dte rows of a chunk; two objects so that reading one chunk's
+    // while the next one's copies are in flight needs no wait for them.
+    __shared__ __align__(16) float tb0[3 * 256], tb1[3 * 256];
+
+    const int H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
+    const int64_t L = p.seqlen;
+
+    // Workgroup -> (b, h); the heads of one sequence run back to back on one
+    // XCD and share its B and C rows through that XCD's L2.
+    const int64_t total = p.batch * H;
+    const int64_t per_xcd = gridDim.x / kXcds;
+    const int64_t logical = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical >= total) return;
+    const int h = (int)(logical % H);
+    const int64_t b = logical / H;
+    const int g = h / HPG;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int il = lane & 15, grp = lane >> 4;
+    const int tile = wide_tile<NIT>(wave), md = tile >> 1;
+    const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
+
+    const uint32_t HP2 = (uint32_t)H * P * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
+    const int64_t hrow = ((b * H + h) * (int64_t)nc) * Q;                 // table row of chunk 0
+    const int64_t hst = (b * H + h) * (int64_t)P * N;                     // this (b, h)'s state
+
+    auto chunk_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
+    // Token rows of chunk c: x and y of head h, B and C of group g.
+    auto x_rows = [&](int c) { return rsrc((const T *)p.x + ((b * L + (int64_t)c * Q) * H + h) * P, chunk_len(c) * HP2); };
+    auto y_rows = [&](int c) { return rsrc((const T *)p.y + ((b * L + (int64_t)c * Q) * H + h) * P, chunk_len(c) * HP2); };
+    auto b_rows = [&](int c) { return rsrc((const T *)p.B + ((b * L + (int64_t)c * Q) * G + g) * N, chunk_len(c) * GN2); };
+    auto c_rows = [&](int c) { return rsrc((const T *)p.C + ((b * L + (int64_t)c * Q) * G + g) * N, chunk_len(c) * GN2); };
+
+    // ---- per-lane offsets, fixed for the whole loop.
+    // Global (bytes): the thread's 16-byte pieces of x and B rows, its C
+    // fragments (row 16 tile + il, columns 8grp + 32ks) and its y values
+    // (row 16 tile + il, columns 4grp + 16q).
+    const uint32_t vx = (uint32_t)(tid / WX) * HP2 + (tid % WX) * 16;
+    const uint32_t vb = (uint32_t)(tid / WB) * GN2 + (tid % WB) * 16;
+    const uint32_t vc = (uint32_t)(16 * tile + il) * GN2 + grp * 16;
+    const uint32_t vy = (uint32_t)(16 * tile + il) * HP2 + grp * 8;
+    // LDS (elements): where those x and B pieces go (piece swizzles depend on
+    // the row modulo 8, the same for all of a thread's pieces).
+    const int lx = (tid / WX) * P + 8 * ((tid % WX) ^ swz_tr<WX>(tid / WX));
+    const int lb = (tid / WB) * N + 8 * ((tid % WB) ^ swz_tr<WB>(tid / WB));
+
+    V8 xr[UXR], br[UBR];
+    Frag<T> cf[KS];  // C rows of the wave's tile (phase A and blue)
+    auto load_x = [&](int c) __attribute__((always_inline)) {
+        const auto r = x_rows(c);
+#pragma unroll
+        for (int u = 0; u < UXR; ++u)
+            xr[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vx, u * RX * HP2, 0));
+    };
+    auto load_b = [&](int c) __attribute__((always_inline)) {
+        const auto r = b_rows(c);
+#pragma unroll
+        for (int u = 0; u < UBR; ++u)
+            br[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vb, u * RB * GN2, 0));
+    };
+    auto load_c = [&](int c) __attribute__((always_inline)) {
+        const auto r = c_rows(c);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc + 64 * ks, 0, 0));
+    };
+    // Table rows of chunk c (one 1 KB copy per table, waves 0-2).
+    auto issue_tables = [&](int c, float *dst) __attribute__((always_inline)) {
+        const int64_t row = hrow + (int64_t)c * Q;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (wave < 3)
+            copy16_to_lds((wave == 0 ? p.cs : wave == 1 ? p.ct : p.dte) + row + 4 * min(ln, Q / 4 - 1),
+                          dst + 256 * wave);
+    };
+
+    // ---- per-lane LDS offsets of the fragment reads (elements).  Every
+    // swizzle period divides 16 (rows) or 8 (tokens), so a fragment address
+    // is a per-lane constant plus a uniform base.
+    // Transposing reads (k = tokens): source lane il = 4kr + a points at
+    // token row 4grp + kr (and +16), columns 16t + 4a .. +3.
+    const int rl = 4 * grp + (il >> 2);
+    int xo[PT];  // x / xd fragments of p tile q
+#pragma unroll
+    for (int q = 0; q < PT; ++q) xo[q] = rl * P + 8 * ((2 * q + ((il & 3) >> 1)) ^ swz_tr<WX>(rl)) + 4 * (il & 1);
+    int xos[PTW];  // xd fragments of the wave's state p tiles
+#pragma unroll
+    for (int q = 0; q < PTW; ++q) {
+        const int t = pw * PTW + q;
+        xos[q] = rl * P + 8 * ((2 * t + ((il & 3) >> 1)) ^ swz_tr<WX>(rl)) + 4 * (il & 1);
+    }
+    int bo[NTW];  // B^T fragments of the wave's state n tiles
+#pragma unroll
+    for (int a = 0; a < NTW; ++a) {
+        const int t = nw * NTW + a;
+        bo[a] = rl * N + 8 * ((2 * t + ((il & 3) >> 1)) ^ swz_tr<WB>(rl)) + 4 * (il & 1);
+    }
+    // 16-byte row reads of B (phase A: rows 16a + il, piece 4ks + grp) and of
+    // h (blue: rows p = 16q + il, piece 4ks + grp).
+    int ro_b[KS], ro_h[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        ro_b[ks] = il * N + 8 * ((4 * ks + grp) ^ swz_tr<WB>(il));
+        ro_h[ks] = il * N + 8 * ((4 * ks + grp) ^ swz_rows16<WB>(il));
+    }
+    auto read_tr = [&](const T *base, int off, int ld) __attribute__((always_inline)) {
+        const i16x4 a0 = ds_read_tr16(base + off);
+        const i16x4 a1 = ds_read_tr16(base + 16 * ld + off);
+        Frag<T> f;
+        f.v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+        return f;
+    };
+
+    // ---- running state, tiles of S^T: hs[a][q][r] = h[p = 16(pw PTW + q) + il][n = 16(nw NTW + a) + 4grp + r]
+    f32x4 hs[NTW][PTW];
+    // Element offsets of the lane's state values within h[P][N], from an
+    // opaque lane index (used rarely; not worth registers across the loop).
+    auto state_offsets = [&](uint32_t (&so)[NTW][PTW]) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q)
+                so[a][q] = (uint32_t)((16 * (pw * PTW + q) + (ln & 15)) * N + 16 * (nw * NTW + a) + 4 * (ln >> 4));
+    };
+    {
+        uint32_t so[NTW][PTW];
+        state_offsets(so);
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q)
+                hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Chunk whose entering state goes to hj (state_out at an index of -1 asks
+    // for the initial state, which enters chunk 0).
+    int cj = -1;
+    if (p.hj && p.state_out_idx) {
+        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[b];
+        cj = j < 0 ? 0 : (int)(min((int64_t)j, L - 1) / Q);
+    }
+    const float dh = p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[h] : 0.f;
+
+    // ---- per-chunk block factors (uniform).
+    float ce[NBLK];   // cs2 at the end of each block
+    float gst[NBLK];  // state Horner factors: exp(cs_e(0)), exp(cs_e(m) - cs_e(m-1))
+    int Qc = 0, nblk = 0;
+    bool live = false, has_prev = false;
+
+    // Switch to chunk c: its x, B and tables have landed (and every wave has
+    // finished chunk c-1's LDS reads).
+    auto enter = [&](int c, const float *tb) __attribute__((always_inline)) {
+        Qc = chunk_len(c);
+        nblk = (Qc + kStep - 1) / kStep;
+        live = 16 * tile < Qc;
+        has_prev = c > 0 || p.init_state != nullptr;
+        // LDS: B rows, x and dte x rows (0 past the sequence), h_{c-1}.
+#pragma unroll
+        for (int u = 0; u < UBR; ++u) *reinterpret_cast<V8 *>(bl + lb + u * RB * N) = br[u];
+#pragma unroll
+        for (int u = 0; u < UXR; ++u) {
+            *reinterpret_cast<V8 *>(xs + lx + u * RX * P) = xr[u];
+            const float d = tb[512 + tid / WX + u * RX];
+            V8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (T)(d * (float)xr[u][e]);
+            *reinterpret_cast<V8 *>(xd + lx + u * RX * P) = v;
+        }
+        if (has_prev) {
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) {
+                    const int pp = 16 * (pw * PTW + q) + il, n = 16 * (nw * NTW + a) + 4 * grp;
+                    *reinterpret_cast<V4 *>(hb + pp * N + 8 * ((n >> 3) ^ swz_rows16<WB>(pp)) + (n & 7)) =
+                        V4{(T)hs[a][q][0], (T)hs[a][q][1], (T)hs[a][q][2], (T)hs[a][q][3]};
+                }
+        }
+        if (c == cj) {
+            uint32_t so[NTW][PTW];
+            state_offsets(so);
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.hj + hst + so[a][q]) = hs[a][q];
+        }
+        // Block factors of the chunk, from the cumsum kernel's table (scalar loads).
+        const __attribute__((address_space(4))) float *bk =
+            (const __attribute__((address_space(4))) float *)(uintptr_t)(p.blk + ((b * H + h) * nc + c) * (int64_t)kBlkStride);
+#pragma unroll
+        for (int m = 0; m < NBLK; ++m) {
+            ce[m] = bk[m];
+            gst[m] = bk[kBlkStride / 2 + m];
+        }
+    };
+
+    // One chunk (tables in tb): blue, orange and D skip, stored; then the state.
+    auto compute = [&](int c, const float *tb) __attribute__((always_inline)) {
+        const float cs2i = tb[16 * tile + il] * kLog2e;
+        f32x4 acc[PT];
+#pragma unroll
+        for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Blue: exp(cs_i) C_i . h_{c-1} (rows p, column i).
+        if (has_prev && live) {
+#pragma unroll
+            for (int q = 0; q < PT; ++q)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    Frag<T> hf;
+                    load8(hf, hb + 16 * q * N + ro_h[ks]);
+                    mma(hf, cf[ks], acc[q]);
+                }
+            const float ei = exp2_hw(cs2i);
+#pragma unroll
+            for (int q = 0; q < PT; ++q) acc[q] = acc[q] * ei;
+        }
+        // G^T of block m, half `half`, for the wave's rows: lane (il, grp)
+        // holds G^T[j][i], i = 16 tile + il, j = 32m + 16half + 4grp + r.
+        auto g_half = [&](int m, int half) __attribute__((always_inline)) {
+            f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Frag<T> bf;
+                load8(bf, bl + (kStep * m + 16 * half) * N + ro_b[ks]);
+                mma(bf, cf[ks], a4);
+            }
+            return a4;
+        };
+        // Orange off the diagonal: G times its row factor
+        // exp2(cs2_i - cs2_e(m)) <= 1, rounded to bf16 once, on dte x.
+        static_for<NBLK - 1>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            if (!live || m >= md) return;
+            const float ai = exp2_hw(cs2i - ce[m]);
+            Frag<T> gf;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x4 a4 = g_half(m, half);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gf.set(4 * half + r, a4[r] * ai);
+            }
+#pragma unroll
+            for (int q = 0; q < PT; ++q) mma(read_tr(xd + kStep * m * P, xo[q], P), gf, acc[q]);
+        });
+        // Diagonal block md: G times the exact factors exp2(cs2_i - ct_j)
+        // (the exponent is at most log2(dt_j) for j <= i; above the diagonal
+        // it is set to -inf, which masks G), plus D at j = i (the skip term),
+        // rounded to bf16 once, on raw x.  j - i = 16 half + r - di, with di
+        // from an opaque copy so that the comparisons are made here and not
+        // kept across the chunk loop.
+        if (live) {
+            int di = 16 * (tile & 1) + il - 4 * grp;
+            asm volatile("" : "+v"(di));
+            const f32x4 ct0 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 4 * grp);
+            const f32x4 ct1 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 16 + 4 * grp);
+            const float ninf = -__builtin_inff();
+            Frag<T> lf;
+            const f32x4 g0 = g_half(md, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = g0[r] * exp2_hw(r > di ? ninf : cs2i - ct0[r]);
+                lf.set(r, r == di ? v + dh : v);
+            }
+            if (tile & 1) {
+                const f32x4 g1 = g_half(md, 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = g1[r] * exp2_hw(16 + r > di ? ninf : cs2i - ct1[r]);
+                    lf.set(4 + r, 16 + r == di ? v + dh : v);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lf.set(4 + r, 0.f);  // rows above the diagonal
+            }
+#pragma unroll
+            for (int q = 0; q < PT; ++q) mma(read_tr(xs + kStep * md * P, xo[q], P), lf, acc[q]);
+        }
+        // y, rounded; rows past the sequence fall outside the buffer.
+        if (live) {
+            const auto r = y_rows(c);
+#pragma unroll
+            for (int q = 0; q < PT; ++q) {
+                const V4 o = V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, vy + 32 * q, 0, 0);
+            }
+        }
+        // C rows of the next chunk (cf is no longer needed).
+        if (c + 1 < nc) load_c(c + 1);
+        // State: h_c = exp(cs_last) h_{c-1} + B^T (w x), Horner over the blocks.
+        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            if (m >= nblk) return;
+            Frag<T> fa[NTW], fb[PTW];
+#pragma unroll
+            for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + kStep * m * N, bo[a], N);
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) fb[q] = read_tr(xd + kStep * m * P, xos[q], P);
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) {
+                    hs[a][q] = hs[a][q] * gst[m];
+                    mma(fa[a], fb[q], hs[a][q]);
+                }
+        });
+    };
+
+    // ---- prologue: chunk 0's inputs.
+    issue_tables(0, tb0);
+    load_x(0);
+    load_b(0);
+    load_c(0);
+    wait_vmcnt<0>();
+    barrier_only();  // every wave's table copies have landed
+    enter(0, tb0);
+    if (nc > 1) {
+        load_x(1);
+        load_b(1);
+        issue_tables(1, tb1);
+    }
+    lds_barrier();
+
+    // ---- chunks, two per iteration so that each table buffer is a
+    // compile-time choice.
+    for (int c0 = 0; c0 < nc; c0 += 2) {
+        static_for<2>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int K = decltype(kc)::value;
+            const int c = c0 + K;
+            if (c >= nc) return;
+            compute(c, K == 0 ? tb0 : tb1);
+            // Chunk c+1's loads and copies were issued before chunk c's C
+            // rows; wait for all of them (after the last chunk too, so that
+            // on every path into the next iteration the C rows have landed
+            // and the compiler adds no wait for them), and for every wave to
+            // finish chunk c's LDS reads.
+            wait_vmcnt<0>();
+            if (c + 1 < nc) {
+                lds_barrier();
+                enter(c + 1, K == 0 ? tb1 : tb0);
+                if (c + 2 < nc) {
+                    load_x(c + 2);
+                    load_b(c + 2);
+                    issue_tables(c + 2, K == 0 ? tb0 : tb1);
+                }
+                lds_barrier();
+            }
+        });
+    }
+    if (p.final_state) {
+        uint32_t so[NTW][PTW];
+        state_offsets(so);
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
+    }
+}
+
+template <int NT, int PT, int NIT>
+hipError_t launch_cfg(const Params &p, hipStream_t stream) {
+    using Cf = FusedCfg<NT, PT, NIT>;
+    if constexpr (!Cf::OK) {
+        return hipErrorNotSupported;
+    } else {
+        const int64_t total = p.batch * p.nheads;
+        const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, NIT>), dim3((unsigned)(per_xcd * kXcds)),
+                           dim3(Cf::THREADS), 0, stream, p);
+        return hipGetLastError();
+    }
+}
+
+template <int NT, int PT>
+hipError_t dispatch_q(const Params &p, hipStream_t stream) {
+    switch (p.chunk) {
+        case 128: return launch_cfg<NT, PT, 8>(p, stream);
+        case 256: return launch_cfg<NT, PT, 16>(p, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+template <int NT>
+hipError_t dispatch_p(const Params &p, hipStream_t stream) {
+    switch (p.headdim) {
+        case 32: return dispatch_q<NT, 2>(p, stream);
+        case 64: return dispatch_q<NT, 4>(p, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream) {
+    // One workgroup per (b, h) and one CU each: with fewer than a CU's worth
+    // of them the chunk-parallel kernels use the GPU better.
+    if (p.batch * p.nheads < kFusedMinHeads) return hipErrorNotSupported;
+    switch (p.dstate) {
+        case 64: return dispatch_p<4>(p, stream);
+        case 128: return dispatch_p<8>(p, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace ssd

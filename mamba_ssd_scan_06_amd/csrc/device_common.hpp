@@ -189,6 +189,21 @@ __device__ __forceinline__ int swz_tr(int r) {
     else return 0;
 }
 
+// 16-row tile of wave w when each of NIT waves owns one tile of a chunk.
+// Waves w, w+4, w+8, w+12 share a SIMD; tile t meets t/2 + 1 causal 32-token
+// blocks, and these orders give every SIMD the same number.
+template <int NIT>
+__device__ __forceinline__ int wide_tile(int w) {
+    if constexpr (NIT == 16) {
+        constexpr unsigned long long map = 0xdcfeab894567'3210ull;  // nibble w = tile of wave w
+        return (int)((map >> (4 * w)) & 15);
+    } else if constexpr (NIT == 8) {
+        return w < 4 ? w : 11 - w;
+    } else {
+        return w;
+    }
+}
+
 // Vector of 8 / 4 elements of T for global <-> register moves.
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> { typedef bf16x8 type; };

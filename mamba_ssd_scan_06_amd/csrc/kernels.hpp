@@ -9,6 +9,8 @@ namespace ssd {
 
 enum class Elem { F32, BF16 };
 
+constexpr int kBlkStride = 16;  // floats per (b, h, c) in the block-factor table
+
 // Everything a kernel needs, passed by value.  Pointers are device pointers
 // with the layouts documented in include/ssd.h; `cs` and `states` point into
 // the caller's workspace.
@@ -30,6 +32,9 @@ struct Params {
     float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
     float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
+    float *blk;               // workspace [b,H,nc,kBlkStride] fp32: per 32-token block m of the chunk,
+                              // [m] = cs*log2(e) at the block's last token, [8+m] = exp(cs_e(m) - cs_e(m-1))
+                              // (exp(cs_e(0)) for m = 0)
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
@@ -47,6 +52,12 @@ hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // shape does not fit its LDS budget (the caller then uses launch_chunk_output).
 hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_at_index(const Params &p, Elem e, hipStream_t stream);
+// Single-pass bf16 forward: one workgroup per (b, h) runs every chunk in
+// order with the state in registers (after launch_chunk_cumsum; writes y,
+// final_state and, with state_out, hj).  Returns hipErrorNotSupported for
+// shapes it does not take or with fewer than kFusedMinHeads (b, h) pairs.
+constexpr int64_t kFusedMinHeads = 256;
+hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream);
 // Whole forward of a one-chunk call of at most 32 tokens in one kernel (y,
 // final_state, state_out; the workspace is not used).  Returns
 // hipErrorNotSupported for other calls and unsupported shapes.

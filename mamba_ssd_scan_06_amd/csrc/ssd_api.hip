@@ -70,7 +70,7 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, ct_off, dte_off, st_off, prev_off, hj_off, total;
+    size_t cs_off, ct_off, dte_off, blk_off, st_off, prev_off, hj_off, total;
     int64_t nc;
 };
 
@@ -84,7 +84,8 @@ Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     L.cs_off = 0;
     L.ct_off = tab_bytes;
     L.dte_off = 2 * tab_bytes;
-    L.st_off = 3 * tab_bytes;
+    L.blk_off = 3 * tab_bytes;
+    L.st_off = L.blk_off + round_up((size_t)s->batch * s->nheads * L.nc * ssd::kBlkStride * sizeof(float));
     L.prev_off = L.st_off + round_up(n_st * sizeof(float));
     L.hj_off = L.prev_off + round_up(n_st * esz);
     L.total = L.nc > 0 ? L.hj_off + round_up(n_hj * sizeof(float)) : 0;
@@ -168,6 +169,7 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     out->cumsum_offset = L.cs_off;
     out->ct_offset = L.ct_off;
     out->dt_decay_offset = L.dte_off;
+    out->block_decay_offset = L.blk_off;
     out->states_offset = L.st_off;
     out->prev_offset = L.prev_off;
     out->hj_offset = L.hj_off;
@@ -251,6 +253,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.cs = ws ? reinterpret_cast<float *>(ws + L.cs_off) : nullptr;
     p.ct = ws ? reinterpret_cast<float *>(ws + L.ct_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
+    p.blk = ws ? reinterpret_cast<float *>(ws + L.blk_off) : nullptr;
     p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
     p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;
     p.hj = ws && state_out ? reinterpret_cast<float *>(ws + L.hj_off) : nullptr;
@@ -275,6 +278,9 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
         // short call: the whole forward in one kernel
     } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
+        const bool fused = e == ssd::Elem::BF16 &&
+                           run.try_step("chunk_scan_fused", [&] { return ssd::launch_chunk_scan_fused(p, stream); });
+        if (!fused) {
         run.step("chunk_state", [&] {
             if (e == ssd::Elem::BF16) {
                 const hipError_t r = ssd::launch_chunk_state_heads(p, stream);
@@ -290,6 +296,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
             }
             return ssd::launch_chunk_output(p, e, stream);
         });
+        }
         if (state_out) run.step("state_at_index", [&] { return ssd::launch_state_at_index(p, e, stream); });
     }
     if (run.err != hipSuccess)

@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 2
+    assert ssd.ssd_abi_version() == 3
 
 
 # ----------------------------------------------------------- full workloads
@@ -306,6 +306,55 @@ def test_in_place_with_state_out(T):
     h = dev["init_state"].clone()
     y, fin, sout = ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], h, 64,
                                           torch.from_numpy(idx).cuda(), final_state=h)
+    torch.cuda.synchronize()
+    check("y", y.float().cpu().numpy(), ref[0], 2e-2)
+    check("final (in place)", h.cpu().numpy(), ref[1], 2e-2)
+    check("state_out", sout.cpu().numpy(), ref[2], 2e-2)
+
+
+# ------------------------------------------------- single-pass fused forward
+# b, T, H, P, N, G, Q, init_state, state_out, D
+FUSED = [
+    (4, 1800, 80, 64, 128, 1, 256, True, True, True),    # the 2.7B layer's configuration, 8 chunks, last of 8
+    (2, 500, 128, 32, 64, 1, 128, True, True, True),     # 4 chunks, last of 116
+    (3, 400, 96, 64, 128, 2, 128, False, True, True),    # two groups, zero start, 4 chunks
+    (4, 200, 64, 64, 128, 1, 256, True, True, False),    # one partial chunk, no D
+    (2, 1024, 128, 64, 64, 4, 256, True, False, True),   # four groups, 4 full chunks
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "b{}_T{}_H{}_P{}_N{}_G{}_Q{}_init{}_sout{}_D{}".format(*c))
+def test_fused_forward(case):
+    b, T, H, P, N, G, Q, init, sout, use_D = case
+    wl = workload("fused", b, T, H, P, N, G, Q, "bf16", init_state=init, state_out=sout, seed=211 + T + H)
+    announce(f"fused forward {wl} D={use_D}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    names = kernel_names(inp, dev=dev)
+    print(f"  kernels: {names}", flush=True)
+    assert "chunk_scan_fused" in names and "chunk_output" not in names
+    got, ref = gpu_run(inp, dev=dev, use_D=use_D), oracle_run(inp, use_D=use_D)
+    check("y", got["y"], ref["y"], TOL["bf16"])
+    check("final_state", got["final"], ref["final"], TOL["bf16"])
+    if sout:
+        check("state_out", got["state_out"], ref["state_out"], TOL["bf16"])
+    again = gpu_run(inp, dev=dev, use_D=use_D)
+    assert np.array_equal(again["y"], got["y"]) and np.array_equal(again["final"], got["final"])
+
+
+def test_fused_in_place():
+    # final_state == init_state through the fused kernel, indices incl. -1.
+    wl = workload("fused_inplace", 4, 450, 64, 64, 64, 1, 128, "bf16", init_state=True, state_out=True, seed=231)
+    announce(f"fused in place {wl}")
+    inp = ssd_inputs.generate(wl)
+    idx = np.array([-1, 0, 200, 449], np.int32)
+    ref = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state, idx)
+    dev = device_inputs(inp)
+    dev["state_out_idx"] = torch.from_numpy(idx).cuda()
+    assert "chunk_scan_fused" in kernel_names(inp, dev=dev)
+    h = dev["init_state"].clone()
+    y, fin, sout = ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], h, 128,
+                                          dev["state_out_idx"], final_state=h)
     torch.cuda.synchronize()
     check("y", y.float().cpu().numpy(), ref[0], 2e-2)
     check("final (in place)", h.cpu().numpy(), ref[1], 2e-2)
