@@ -63,7 +63,7 @@ struct FusedCfg {
     static constexpr int UXR = Q * WX / THREADS;                 // 16-byte x pieces per thread
     static constexpr int UBR = Q * WB / THREADS;                 // 16-byte B pieces per thread
     static constexpr size_t LDS_BYTES =
-        (size_t)Q * N * 2 + 2 * (size_t)Q * P * 2 + (size_t)P * N * 2 + 2 * 3 * 256 * 4;
+        (size_t)Q * N * 2 + 2 * (size_t)Q * P * 2 + (size_t)P * N * 2 + 2 * 4 * 256 * 4;
     static constexpr bool OK = NIT >= 8 && NT >= 2 && NT % WPN == 0 && PT % WPP == 0 && PTW >= 1 &&
                                (Q * WX) % THREADS == 0 && UXR >= 1 && (Q * WB) % THREADS == 0 &&
                                LDS_BYTES <= 160 * 1024;
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     __shared__ __align__(16) T hb[P * N];   // h_{c-1} rows p, pieces swizzled for 16-byte reads
     // cs, ct, dte rows of a chunk; two objects so that reading one chunk's
     // while the next one's copies are in flight needs no wait for them.
-    __shared__ __align__(16) float tb0[3 * 256], tb1[3 * 256];
+    // (and the block factors, in the fourth 1 KB row).
+    __shared__ __align__(16) float tb0[4 * 256], tb1[4 * 256];
 
     const int H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
     const int64_t L = p.seqlen;
@@ -162,7 +163,9 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         for (int ks = 0; ks < KS; ++ks)
             cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc + 64 * ks, 0, 0));
     };
-    // Table rows of chunk c (one 1 KB copy per table, waves 0-2).
+    // Table rows of chunk c (one 1 KB copy per table, waves 0-2) and its
+    // block factors (64 bytes, wave 3; its other lanes repeat the last piece).
+    static_assert(Cf::W >= 4, "four waves copy the tables");
     auto issue_tables = [&](int c, float *dst) __attribute__((always_inline)) {
         const int64_t row = hrow + (int64_t)c * Q;
         int ln = lane;
@@ -170,6 +173,9 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         if (wave < 3)
             copy16_to_lds((wave == 0 ? p.cs : wave == 1 ? p.ct : p.dte) + row + 4 * min(ln, Q / 4 - 1),
                           dst + 256 * wave);
+        else if (wave == 3)
+            copy16_to_lds(p.blk + ((b * H + h) * nc + c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
+                          dst + 768);
     };
 
     // ---- per-lane LDS offsets of the fragment reads (elements).  Every
@@ -260,7 +266,9 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < UXR; ++u) {
             *reinterpret_cast<V8 *>(xs + lx + u * RX * P) = xr[u];
-            const float d = tb[512 + tid / WX + u * RX];
+            int t = tid;  // opaque copy: the row index is recomputed here, not kept (or spilled)
+            asm volatile("" : "+v"(t));
+            const float d = tb[512 + t / WX + u * RX];
             V8 v;
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = (T)(d * (float)xr[u][e]);
@@ -284,13 +292,11 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
 #pragma unroll
                 for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.hj + hst + so[a][q]) = hs[a][q];
         }
-        // Block factors of the chunk, from the cumsum kernel's table (scalar loads).
-        const __attribute__((address_space(4))) float *bk =
-            (const __attribute__((address_space(4))) float *)(uintptr_t)(p.blk + ((b * H + h) * nc + c) * (int64_t)kBlkStride);
+        // Block factors of the chunk (copied with the tables; uniform).
 #pragma unroll
         for (int m = 0; m < NBLK; ++m) {
-            ce[m] = bk[m];
-            gst[m] = bk[kBlkStride / 2 + m];
+            ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[768 + m])));
+            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[768 + kBlkStride / 2 + m])));
         }
     };
 
@@ -351,8 +357,10 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         if (live) {
             int di = 16 * (tile & 1) + il - 4 * grp;
             asm volatile("" : "+v"(di));
-            const f32x4 ct0 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 4 * grp);
-            const f32x4 ct1 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 16 + 4 * grp);
+            int g4 = 4 * grp;  // opaque: recomputed here rather than kept (or spilled) across the loop
+            asm volatile("" : "+v"(g4));
+            const f32x4 ct0 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + g4);
+            const f32x4 ct1 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 16 + g4);
             const float ninf = -__builtin_inff();
             Frag<T> lf;
             const f32x4 g0 = g_half(md, 0);
