@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -110,7 +110,15 @@ typedef struct {
  *            rounded to nearest even to dtype; entry 0 is written only when
  *            init_state is given (otherwise it is zero and left unwritten).
  *   hj       fp32 [batch, nheads, headdim, dstate]: the state entering the
- *            chunk that holds state_out_idx[b] (written only with state_out). */
+ *            chunk that holds state_out_idx[b] (written only with state_out).
+ *   sync     int32 [2 + batch*nheads]: a time-out word (nonzero if a wait of
+ *            the single-pass kernel for a state handed over by another
+ *            workgroup gave up, which only a fault elsewhere can cause;
+ *            outputs are then unspecified) and one hand-off flag per (b, h);
+ *            cleared by the first kernel of each call.  The single-pass
+ *            kernel hands a state over through the states region (entry
+ *            [b, 0, h]) when it splits a sequence's chunks between two
+ *            workgroups. */
 typedef struct {
     size_t cumsum_offset;
     size_t ct_offset;
@@ -119,6 +127,7 @@ typedef struct {
     size_t states_offset;
     size_t prev_offset;
     size_t hj_offset;
+    size_t sync_offset;
     size_t total_bytes;
     int64_t nchunks;
 } ssd_workspace_layout;

@@ -40,7 +40,7 @@ class ssd_workspace_layout(ctypes.Structure):
                 ("dt_decay_offset", ctypes.c_size_t), ("block_decay_offset", ctypes.c_size_t),
                 ("states_offset", ctypes.c_size_t),
                 ("prev_offset", ctypes.c_size_t), ("hj_offset", ctypes.c_size_t),
-                ("total_bytes", ctypes.c_size_t),
+                ("sync_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
                 ("nchunks", ctypes.c_int64)]
 
 

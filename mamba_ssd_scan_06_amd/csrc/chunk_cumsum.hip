@@ -72,6 +72,12 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
     __syncthreads();
     const int h = h0 + wave;
     if (h >= H) return;
+    // Clear the single-pass kernel's hand-off flag of (b, h) and the time-out
+    // word for the kernel that follows.
+    if (p.sync && c == 0 && lane == 0) {
+        p.sync[kSyncHeader + b * H + h] = 0;
+        if (b == 0 && h == 0) p.sync[1] = 0;
+    }
 
     // Tokens i = VPT*lane + v (lanes past the chunk hold zeros and store nothing).
     const int i0 = VPT * lane;

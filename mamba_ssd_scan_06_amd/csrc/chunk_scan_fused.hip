@@ -50,6 +50,20 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kStep = 32;  // tokens per j block
+constexpr int kSpinLimit = 1 << 20;  // polls before a hand-off wait gives up (well over 0.1 s)
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 template <int NT, int PT, int NIT>
 struct FusedCfg {
@@ -103,15 +117,57 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
     const int64_t L = p.seqlen;
 
-    // Workgroup -> (b, h); the heads of one sequence run back to back on one
-    // XCD and share its B and C rows through that XCD's L2.
-    const int64_t total = p.batch * H;
-    const int64_t per_xcd = gridDim.x / kXcds;
-    const int64_t logical = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (logical >= total) return;
-    const int h = (int)(logical % H);
-    const int64_t b = logical / H;
-    const int g = h / HPG;
+    // ---- work of this workgroup (one per CU, persistent).  A unit is the
+    // chunks [cb, ce) of one (b, h) pair ("item" b*H + h).  Workgroups are
+    // dealt to the XCDs in turn (w % 8), and each XCD takes a contiguous
+    // range of items, so that the heads sharing B and C rows run on one
+    // XCD and share its L2.  Within an XCD, with Ix items on Wx workgroups,
+    // each takes F = Ix / Wx whole items; the R = Ix % Wx left over are cut
+    // in two halves of their chunks when 2R <= Wx: workgroups 0..R-1 run a
+    // first half before their whole items, workgroups R..2R-1 a second half
+    // after theirs, taking the state entering it from the first half
+    // (written long before it is needed).  Every workgroup then runs F or
+    // F + 1/2 items' chunks instead of F or F + 1.
+    const int Wg = gridDim.x;
+    const int NX = Wg % kXcds == 0 ? kXcds : 1;
+    const int xcd = (int)blockIdx.x % NX, w = (int)blockIdx.x / NX, Wx = Wg / NX;
+    const int64_t I = p.batch * H;
+    const int64_t Ibase = I / NX, Iext = I % NX;
+    const int64_t Ix = Ibase + (xcd < Iext ? 1 : 0);
+    const int64_t ibeg = xcd * Ibase + min((int64_t)xcd, Iext);  // first item of this XCD
+    const int F = (int)(Ix / Wx), R = (int)(Ix - (int64_t)F * Wx);
+    const bool split = F >= 1 && R > 0 && 2 * R <= Wx && nc >= 2;
+    const int nch = nc / 2;
+    const int nunits = F + (split ? (w < 2 * R ? 1 : 0) : (w < R ? 1 : 0));
+    struct Unit {
+        int64_t item;
+        int cb, ce;
+    };
+    auto unit = [&](int k) -> Unit {
+        if (split && w < R) {
+            if (k == 0) return Unit{ibeg + (int64_t)F * Wx + w, 0, nch};
+            return Unit{ibeg + w + (int64_t)Wx * (k - 1), 0, nc};
+        }
+        if (split && w < 2 * R && k == F) return Unit{ibeg + (int64_t)F * Wx + (w - R), nch, nc};
+        return Unit{ibeg + w + (int64_t)Wx * k, 0, nc};
+    };
+    if (nunits == 0) return;
+    // A step is one chunk of one unit; steps run in order k, then c.
+    struct Step {
+        int k, c;
+        int64_t item;
+        int cb, ce;
+    };
+    auto step_of = [&](int k, int c) -> Step {
+        const Unit u = unit(k);
+        return Step{k, c, u.item, u.cb, u.ce};
+    };
+    auto next_step = [&](const Step &st) -> Step {
+        if (st.c + 1 < st.ce) return Step{st.k, st.c + 1, st.item, st.cb, st.ce};
+        return step_of(st.k + 1, unit(st.k + 1).cb);
+    };
+    int nsteps = 0;
+    for (int k = 0; k < nunits; ++k) nsteps += unit(k).ce - unit(k).cb;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -120,15 +176,25 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
     const uint32_t HP2 = (uint32_t)H * P * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
-    const int64_t hrow = ((b * H + h) * (int64_t)nc) * Q;                 // table row of chunk 0
-    const int64_t hst = (b * H + h) * (int64_t)P * N;                     // this (b, h)'s state
+    // Item -> sequence, head, group.
+    auto seq_of = [&](int64_t it) { return it / H; };
+    auto head_of = [&](int64_t it) { return (int)(it % H); };
+    auto group_of = [&](int64_t it) { return (int)(it % H) / HPG; };
 
     auto chunk_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
-    // Token rows of chunk c: x and y of head h, B and C of group g.
-    auto x_rows = [&](int c) { return rsrc((const T *)p.x + ((b * L + (int64_t)c * Q) * H + h) * P, chunk_len(c) * HP2); };
-    auto y_rows = [&](int c) { return rsrc((const T *)p.y + ((b * L + (int64_t)c * Q) * H + h) * P, chunk_len(c) * HP2); };
-    auto b_rows = [&](int c) { return rsrc((const T *)p.B + ((b * L + (int64_t)c * Q) * G + g) * N, chunk_len(c) * GN2); };
-    auto c_rows = [&](int c) { return rsrc((const T *)p.C + ((b * L + (int64_t)c * Q) * G + g) * N, chunk_len(c) * GN2); };
+    // Token rows of chunk c of item it: x and y of its head, B and C of its group.
+    auto x_rows = [&](int64_t it, int c) {
+        return rsrc((const T *)p.x + ((seq_of(it) * L + (int64_t)c * Q) * H + head_of(it)) * P, chunk_len(c) * HP2);
+    };
+    auto y_rows = [&](int64_t it, int c) {
+        return rsrc((const T *)p.y + ((seq_of(it) * L + (int64_t)c * Q) * H + head_of(it)) * P, chunk_len(c) * HP2);
+    };
+    auto b_rows = [&](int64_t it, int c) {
+        return rsrc((const T *)p.B + ((seq_of(it) * L + (int64_t)c * Q) * G + group_of(it)) * N, chunk_len(c) * GN2);
+    };
+    auto c_rows = [&](int64_t it, int c) {
+        return rsrc((const T *)p.C + ((seq_of(it) * L + (int64_t)c * Q) * G + group_of(it)) * N, chunk_len(c) * GN2);
+    };
 
     // ---- per-lane offsets, fixed for the whole loop.
     // Global (bytes): the thread's 16-byte pieces of x and B rows, its C
@@ -145,20 +211,20 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
 
     V8 xr[UXR], br[UBR];
     Frag<T> cf[KS];  // C rows of the wave's tile (phase A and blue)
-    auto load_x = [&](int c) __attribute__((always_inline)) {
-        const auto r = x_rows(c);
+    auto load_x = [&](const Step &st) __attribute__((always_inline)) {
+        const auto r = x_rows(st.item, st.c);
 #pragma unroll
         for (int u = 0; u < UXR; ++u)
             xr[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vx, u * RX * HP2, 0));
     };
-    auto load_b = [&](int c) __attribute__((always_inline)) {
-        const auto r = b_rows(c);
+    auto load_b = [&](const Step &st) __attribute__((always_inline)) {
+        const auto r = b_rows(st.item, st.c);
 #pragma unroll
         for (int u = 0; u < UBR; ++u)
             br[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vb, u * RB * GN2, 0));
     };
-    auto load_c = [&](int c) __attribute__((always_inline)) {
-        const auto r = c_rows(c);
+    auto load_c = [&](const Step &st) __attribute__((always_inline)) {
+        const auto r = c_rows(st.item, st.c);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc + 64 * ks, 0, 0));
@@ -166,15 +232,15 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     // Table rows of chunk c (one 1 KB copy per table, waves 0-2) and its
     // block factors (64 bytes, wave 3; its other lanes repeat the last piece).
     static_assert(Cf::W >= 4, "four waves copy the tables");
-    auto issue_tables = [&](int c, float *dst) __attribute__((always_inline)) {
-        const int64_t row = hrow + (int64_t)c * Q;
+    auto issue_tables = [&](const Step &st, float *dst) __attribute__((always_inline)) {
+        const int64_t row = (st.item * nc + st.c) * (int64_t)Q;  // tables are [b,H,nc,Q]: item-major
         int ln = lane;
         asm volatile("" : "+v"(ln));
         if (wave < 3)
             copy16_to_lds((wave == 0 ? p.cs : wave == 1 ? p.ct : p.dte) + row + 4 * min(ln, Q / 4 - 1),
                           dst + 256 * wave);
         else if (wave == 3)
-            copy16_to_lds(p.blk + ((b * H + h) * nc + c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
+            copy16_to_lds(p.blk + (st.item * nc + st.c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
                           dst + 768);
     };
 
@@ -228,24 +294,72 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
             for (int q = 0; q < PTW; ++q)
                 so[a][q] = (uint32_t)((16 * (pw * PTW + q) + (ln & 15)) * N + 16 * (nw * NTW + a) + 4 * (ln >> 4));
     };
-    {
+    // The (b, h) state handed from a first half to a second half: entry
+    // [b, 0, h] of the workspace's chunk-state region, and its flag.
+    auto handoff_rsrc = [&](int64_t it) {
+        return buffer_rsrc(p.states + ((seq_of(it) * nc) * H + head_of(it)) * (int64_t)P * N, (uint32_t)(P * N * 4));
+    };
+    int *handoff_flag = p.sync + kSyncHeader;
+    bool gave_up = false;  // a hand-off wait timed out (the wave waits no more)
+    // Start a unit: h_{cb-1} is the initial state (or 0) for cb = 0, else
+    // the state the first half handed over.
+    auto begin_unit = [&](const Step &st) __attribute__((always_inline)) {
         uint32_t so[NTW][PTW];
         state_offsets(so);
+        const int64_t hst = st.item * (int64_t)P * N;
+        if (st.cb == 0) {
 #pragma unroll
-        for (int a = 0; a < NTW; ++a)
+            for (int a = 0; a < NTW; ++a)
 #pragma unroll
-            for (int q = 0; q < PTW; ++q)
-                hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+                for (int q = 0; q < PTW; ++q)
+                    hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            if (!gave_up && !wait_flag_device(handoff_flag + st.item, kSpinLimit)) {
+                gave_up = true;
+                set_flag_device(p.sync + 1, 1);
+            }
+            const auto r = handoff_rsrc(st.item);
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) hs[a][q] = load_f4_device(r, 4 * so[a][q]);
+        }
+    };
+    // End a unit (hs = h_{ce-1}): the final state, or the hand-off.
+    auto end_unit = [&](const Step &st) __attribute__((always_inline)) {
+        uint32_t so[NTW][PTW];
+        state_offsets(so);
+        if (st.ce == nc) {
+            if (p.final_state) {
+                const int64_t hst = st.item * (int64_t)P * N;
+#pragma unroll
+                for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                    for (int q = 0; q < PTW; ++q)
+                        *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
+            }
+        } else {
+            const auto r = handoff_rsrc(st.item);
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) store_f4_device(r, 4 * so[a][q], hs[a][q]);
+            wait_vmcnt<0>();  // every store of this wave is visible device-wide ...
+            barrier_only();   // ... and of every wave
+            if (wave == 0) set_flag_device(handoff_flag + st.item, 1);
+        }
+    };
     // Chunk whose entering state goes to hj (state_out at an index of -1 asks
-    // for the initial state, which enters chunk 0).
-    int cj = -1;
-    if (p.hj && p.state_out_idx) {
-        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[b];
-        cj = j < 0 ? 0 : (int)(min((int64_t)j, L - 1) / Q);
-    }
-    const float dh = p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[h] : 0.f;
+    // for the initial state, which enters chunk 0), and the skip weight.
+    auto cj_of = [&](int64_t it) {
+        if (!(p.hj && p.state_out_idx)) return -1;
+        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[seq_of(it)];
+        return j < 0 ? 0 : (int)(min((int64_t)j, L - 1) / Q);
+    };
+    auto dh_of = [&](int64_t it) {
+        return p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[head_of(it)] : 0.f;
+    };
 
     // ---- per-chunk block factors (uniform).
     float ce[NBLK];   // cs2 at the end of each block
@@ -255,7 +369,8 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
 
     // Switch to chunk c: its x, B and tables have landed (and every wave has
     // finished chunk c-1's LDS reads).
-    auto enter = [&](int c, const float *tb) __attribute__((always_inline)) {
+    auto enter = [&](const Step &st, const float *tb) __attribute__((always_inline)) {
+        const int c = st.c;
         Qc = chunk_len(c);
         nblk = (Qc + kStep - 1) / kStep;
         live = 16 * tile < Qc;
@@ -284,9 +399,10 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                         V4{(T)hs[a][q][0], (T)hs[a][q][1], (T)hs[a][q][2], (T)hs[a][q][3]};
                 }
         }
-        if (c == cj) {
+        if (c == cj_of(st.item)) {
             uint32_t so[NTW][PTW];
             state_offsets(so);
+            const int64_t hst = st.item * (int64_t)P * N;
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -301,7 +417,9 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     };
 
     // One chunk (tables in tb): blue, orange and D skip, stored; then the state.
-    auto compute = [&](int c, const float *tb) __attribute__((always_inline)) {
+    auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb) __attribute__((always_inline)) {
+        const int c = st.c;
+        const float dh = dh_of(st.item);
         const float cs2i = tb[16 * tile + il] * kLog2e;
         f32x4 acc[PT];
 #pragma unroll
@@ -385,7 +503,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         }
         // y, rounded; rows past the sequence fall outside the buffer.
         if (live) {
-            const auto r = y_rows(c);
+            const auto r = y_rows(st.item, c);
 #pragma unroll
             for (int q = 0; q < PT; ++q) {
                 const V4 o = V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]};
@@ -393,7 +511,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
             }
         }
         // C rows of the next chunk (cf is no longer needed).
-        if (c + 1 < nc) load_c(c + 1);
+        if (has_next) load_c(nx);
         // State: h_c = exp(cs_last) h_{c-1} + B^T (w x), Horner over the blocks.
         static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
@@ -413,54 +531,54 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         });
     };
 
-    // ---- prologue: chunk 0's inputs.
-    issue_tables(0, tb0);
-    load_x(0);
-    load_b(0);
-    load_c(0);
+    // ---- prologue: the first step's inputs.
+    Step cur = step_of(0, unit(0).cb);
+    issue_tables(cur, tb0);
+    load_x(cur);
+    load_b(cur);
+    load_c(cur);
     wait_vmcnt<0>();
     barrier_only();  // every wave's table copies have landed
-    enter(0, tb0);
-    if (nc > 1) {
-        load_x(1);
-        load_b(1);
-        issue_tables(1, tb1);
+    begin_unit(cur);
+    enter(cur, tb0);
+    if (nsteps > 1) {
+        const Step nx = next_step(cur);
+        load_x(nx);
+        load_b(nx);
+        issue_tables(nx, tb1);
     }
     lds_barrier();
 
-    // ---- chunks, two per iteration so that each table buffer is a
+    // ---- steps, two per iteration so that each table buffer is a
     // compile-time choice.
-    for (int c0 = 0; c0 < nc; c0 += 2) {
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
         static_for<2>([&](auto kc) __attribute__((always_inline)) {
             constexpr int K = decltype(kc)::value;
-            const int c = c0 + K;
-            if (c >= nc) return;
-            compute(c, K == 0 ? tb0 : tb1);
-            // Chunk c+1's loads and copies were issued before chunk c's C
-            // rows; wait for all of them (after the last chunk too, so that
-            // on every path into the next iteration the C rows have landed
-            // and the compiler adds no wait for them), and for every wave to
-            // finish chunk c's LDS reads.
+            const int s = s0 + K;
+            if (s >= nsteps) return;
+            const bool has_next = s + 1 < nsteps;
+            const Step nx = has_next ? next_step(cur) : cur;
+            compute(cur, has_next, nx, K == 0 ? tb0 : tb1);
+            // The next step's loads and copies were issued before this
+            // step's C rows; wait for all of them (after the last step too,
+            // so that on every path into the next iteration the C rows have
+            // landed and the compiler adds no wait for them).
             wait_vmcnt<0>();
-            if (c + 1 < nc) {
-                lds_barrier();
-                enter(c + 1, K == 0 ? tb1 : tb0);
-                if (c + 2 < nc) {
-                    load_x(c + 2);
-                    load_b(c + 2);
-                    issue_tables(c + 2, K == 0 ? tb0 : tb1);
+            if (cur.c + 1 == cur.ce) end_unit(cur);
+            if (has_next) {
+                lds_barrier();  // every wave has finished this step's LDS reads
+                if (nx.c == nx.cb) begin_unit(nx);
+                enter(nx, K == 0 ? tb1 : tb0);
+                if (s + 2 < nsteps) {
+                    const Step nn = next_step(nx);
+                    load_x(nn);
+                    load_b(nn);
+                    issue_tables(nn, K == 0 ? tb0 : tb1);
                 }
                 lds_barrier();
+                cur = nx;
             }
         });
-    }
-    if (p.final_state) {
-        uint32_t so[NTW][PTW];
-        state_offsets(so);
-#pragma unroll
-        for (int a = 0; a < NTW; ++a)
-#pragma unroll
-            for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
     }
 }
 
@@ -470,10 +588,11 @@ hipError_t launch_cfg(const Params &p, hipStream_t stream) {
     if constexpr (!Cf::OK) {
         return hipErrorNotSupported;
     } else {
-        const int64_t total = p.batch * p.nheads;
-        const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, NIT>), dim3((unsigned)(per_xcd * kXcds)),
-                           dim3(Cf::THREADS), 0, stream, p);
+        // One workgroup per CU (each takes one CU's LDS); never more than items.
+        const int64_t items = p.batch * p.nheads;
+        const int64_t grid = std::min<int64_t>(items, compute_units());
+        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, NIT>), dim3((unsigned)grid), dim3(Cf::THREADS), 0,
+                           stream, p);
         return hipGetLastError();
     }
 }

@@ -189,6 +189,46 @@ __device__ __forceinline__ int swz_tr(int r) {
     else return 0;
 }
 
+// Data handed from one workgroup to another that may run on a different
+// XCD.  Each XCD has its own L2, and for ordinary device memory the L2s are
+// not kept coherent with each other, so these accesses carry the device-scope
+// cache-policy bit (sc1): loads read from the memory side instead of a
+// possibly stale line of this XCD's L2, stores write through to it.  A store
+// counts as complete (vmcnt) once it is visible device-wide, so a wave that
+// waits for its stores and then stores a flag with device scope publishes the
+// data before the flag; a reader polls the flag with device scope and only
+// then issues its loads.
+constexpr int kScDevice = 16;  // cache-policy operand of the buffer builtins: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    // Raw buffer (stride 0); word 3 selects 32-bit data, the gfx9 value for untyped accesses.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 load_f4_device(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kScDevice));
+}
+__device__ __forceinline__ void store_f4_device(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, const f32x4 &v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, kScDevice);
+}
+// Polls a device-scope flag until it is nonzero (the same value for every
+// lane).  Gives up after `limit` polls and returns false, so that a wait can
+// never hang the GPU.
+__device__ __forceinline__ bool wait_flag_device(const int *flag, int limit) {
+    for (int k = 0; k < limit; ++k) {
+        const int v = __hip_atomic_load(const_cast<int *>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readfirstlane(v) != 0) {
+            // Later loads stay after the poll in program order.
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+__device__ __forceinline__ void set_flag_device(int *flag, int v) {
+    __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // 16-row tile of wave w when each of NIT waves owns one tile of a chunk.
 // Waves w, w+4, w+8, w+12 share a SIMD; tile t meets t/2 + 1 causal 32-token
 // blocks, and these orders give every SIMD the same number.

@@ -10,6 +10,8 @@ namespace ssd {
 enum class Elem { F32, BF16 };
 
 constexpr int kBlkStride = 16;  // floats per (b, h, c) in the block-factor table
+constexpr int kSyncHeader = 2;  // words before the hand-off flags in the sync region
+inline int64_t sync_words(int64_t batch, int64_t nheads) { return kSyncHeader + batch * nheads; }
 
 // Everything a kernel needs, passed by value.  Pointers are device pointers
 // with the layouts documented in include/ssd.h; `cs` and `states` point into
@@ -32,6 +34,8 @@ struct Params {
     float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
     float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
+    int *sync;                // workspace int32 [2 + b*H]: [0] unused, [1] wait time-out word, then one
+                              // hand-off flag per (b, h) of the single-pass kernel
     float *blk;               // workspace [b,H,nc,kBlkStride] fp32: per 32-token block m of the chunk,
                               // [m] = cs*log2(e) at the block's last token, [8+m] = exp(cs_e(m) - cs_e(m-1))
                               // (exp(cs_e(0)) for m = 0)

@@ -70,7 +70,7 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, ct_off, dte_off, blk_off, st_off, prev_off, hj_off, total;
+    size_t cs_off, ct_off, dte_off, blk_off, st_off, prev_off, hj_off, sync_off, total;
     int64_t nc;
 };
 
@@ -88,7 +88,8 @@ Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     L.st_off = L.blk_off + round_up((size_t)s->batch * s->nheads * L.nc * ssd::kBlkStride * sizeof(float));
     L.prev_off = L.st_off + round_up(n_st * sizeof(float));
     L.hj_off = L.prev_off + round_up(n_st * esz);
-    L.total = L.nc > 0 ? L.hj_off + round_up(n_hj * sizeof(float)) : 0;
+    L.sync_off = L.hj_off + round_up(n_hj * sizeof(float));
+    L.total = L.nc > 0 ? L.sync_off + round_up((size_t)ssd::sync_words(s->batch, s->nheads) * sizeof(int32_t)) : 0;
     return L;
 }
 
@@ -173,6 +174,7 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     out->states_offset = L.st_off;
     out->prev_offset = L.prev_off;
     out->hj_offset = L.hj_off;
+    out->sync_offset = L.sync_off;
     out->total_bytes = L.total;
     out->nchunks = L.nc;
     return SSD_OK;
@@ -254,6 +256,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.ct = ws ? reinterpret_cast<float *>(ws + L.ct_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
     p.blk = ws ? reinterpret_cast<float *>(ws + L.blk_off) : nullptr;
+    p.sync = ws ? reinterpret_cast<int *>(ws + L.sync_off) : nullptr;
     p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
     p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;
     p.hj = ws && state_out ? reinterpret_cast<float *>(ws + L.hj_off) : nullptr;

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ssd.ssd_abi_version() == 3
+    assert ssd.ssd_abi_version() == 4
 
 
 def test_status_strings():
@@ -54,6 +54,7 @@ def test_workspace_bytes_formula():
     n_st = 2 * nc * 4 * 64 * 128             # states, prev: [b,nc,H,P,N]
     n_hj = 2 * 4 * 64 * 128                  # hj: [b,H,P,N]
     n_blk = 2 * 4 * nc * 16                  # block_decay: [b,H,nc,16]
+    n_sync = 2 + 2 * 4                       # sync: time-out word + header, one flag per (b, h)
     rnd = lambda v: (v + 255) // 256 * 256
     lay = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_BF16)
     assert lay.nchunks == nc and lay.cumsum_offset == 0
@@ -62,11 +63,12 @@ def test_workspace_bytes_formula():
     assert lay.states_offset == 3 * rnd(tab) + rnd(4 * n_blk)
     assert lay.prev_offset == lay.states_offset + rnd(4 * n_st)
     assert lay.hj_offset == lay.prev_offset + rnd(2 * n_st)
-    assert lay.total_bytes == lay.hj_offset + rnd(4 * n_hj)
+    assert lay.sync_offset == lay.hj_offset + rnd(4 * n_hj)
+    assert lay.total_bytes == lay.sync_offset + rnd(4 * n_sync)
     assert ssd.ssd_workspace_bytes(s, 64, ssd.SSD_DTYPE_BF16) == lay.total_bytes
     lay32 = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_F32)
     assert lay32.hj_offset == lay32.prev_offset + rnd(4 * n_st)
-    assert lay32.total_bytes == 3 * rnd(tab) + rnd(4 * n_blk) + 2 * rnd(4 * n_st) + rnd(4 * n_hj)
+    assert lay32.total_bytes == 3 * rnd(tab) + rnd(4 * n_blk) + 2 * rnd(4 * n_st) + rnd(4 * n_hj) + rnd(4 * n_sync)
     assert ssd.ssd_workspace_bytes(shape(T=0), 64, ssd.SSD_DTYPE_BF16) == 0
 
 

@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 3
+    assert ssd.ssd_abi_version() == 4
 
 
 # ----------------------------------------------------------- full workloads
@@ -320,6 +320,9 @@ FUSED = [
     (3, 400, 96, 64, 128, 2, 128, False, True, True),    # two groups, zero start, 4 chunks
     (4, 200, 64, 64, 128, 1, 256, True, True, False),    # one partial chunk, no D
     (2, 1024, 128, 64, 64, 4, 256, True, False, True),   # four groups, 4 full chunks
+    # Work split over a persistent grid of one workgroup per CU (256 here):
+    (2, 300, 200, 64, 64, 1, 128, True, True, True),     # 400 pairs: 144 left over, too many to split
+    (3, 700, 96, 64, 128, 1, 256, True, True, True),     # 288 pairs: 32 split in halves of 3 chunks (1 + 2)
 ]
 
 
@@ -333,12 +336,15 @@ def test_fused_forward(case):
     names = kernel_names(inp, dev=dev)
     print(f"  kernels: {names}", flush=True)
     assert "chunk_scan_fused" in names and "chunk_output" not in names
-    got, ref = gpu_run(inp, dev=dev, use_D=use_D), oracle_run(inp, use_D=use_D)
+    got, ref = gpu_run(inp, dev=dev, use_D=use_D, return_workspace=True), oracle_run(inp, use_D=use_D)
+    assert got["timeout"] == 0
     check("y", got["y"], ref["y"], TOL["bf16"])
     check("final_state", got["final"], ref["final"], TOL["bf16"])
     if sout:
         check("state_out", got["state_out"], ref["state_out"], TOL["bf16"])
-    again = gpu_run(inp, dev=dev, use_D=use_D)
+    # Run again on a fresh workspace filled with nonzero bytes (hand-off flags
+    # must be cleared by the call itself): the same bits.
+    again = gpu_run(inp, dev=dev, use_D=use_D, fill_workspace=0xFF)
     assert np.array_equal(again["y"], got["y"]) and np.array_equal(again["final"], got["final"])
 
 
