@@ -153,17 +153,26 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     };
     if (nunits == 0) return;
     // A step is one chunk of one unit; steps run in order k, then c.
+    // (b, h, g of the item are worked out once per unit; items fit 32 bits
+    // since batch and nheads are at most 65535.)
     struct Step {
         int k, c;
         int64_t item;
         int cb, ce;
+        int64_t b;
+        int h, g;
     };
     auto step_of = [&](int k, int c) -> Step {
         const Unit u = unit(k);
-        return Step{k, c, u.item, u.cb, u.ce};
+        const uint32_t it = (uint32_t)u.item, hh = it % (uint32_t)H;
+        return Step{k, c, u.item, u.cb, u.ce, (int64_t)(it / (uint32_t)H), (int)hh, (int)hh / HPG};
     };
     auto next_step = [&](const Step &st) -> Step {
-        if (st.c + 1 < st.ce) return Step{st.k, st.c + 1, st.item, st.cb, st.ce};
+        if (st.c + 1 < st.ce) {
+            Step n = st;
+            n.c = st.c + 1;
+            return n;
+        }
         return step_of(st.k + 1, unit(st.k + 1).cb);
     };
     int nsteps = 0;
@@ -176,24 +185,19 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
     const uint32_t HP2 = (uint32_t)H * P * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
-    // Item -> sequence, head, group.
-    auto seq_of = [&](int64_t it) { return it / H; };
-    auto head_of = [&](int64_t it) { return (int)(it % H); };
-    auto group_of = [&](int64_t it) { return (int)(it % H) / HPG; };
-
     auto chunk_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
-    // Token rows of chunk c of item it: x and y of its head, B and C of its group.
-    auto x_rows = [&](int64_t it, int c) {
-        return rsrc((const T *)p.x + ((seq_of(it) * L + (int64_t)c * Q) * H + head_of(it)) * P, chunk_len(c) * HP2);
+    // Token rows of a step's chunk: x and y of its head, B and C of its group.
+    auto x_rows = [&](const Step &st) {
+        return rsrc((const T *)p.x + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * P, chunk_len(st.c) * HP2);
     };
-    auto y_rows = [&](int64_t it, int c) {
-        return rsrc((const T *)p.y + ((seq_of(it) * L + (int64_t)c * Q) * H + head_of(it)) * P, chunk_len(c) * HP2);
+    auto y_rows = [&](const Step &st) {
+        return rsrc((const T *)p.y + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * P, chunk_len(st.c) * HP2);
     };
-    auto b_rows = [&](int64_t it, int c) {
-        return rsrc((const T *)p.B + ((seq_of(it) * L + (int64_t)c * Q) * G + group_of(it)) * N, chunk_len(c) * GN2);
+    auto b_rows = [&](const Step &st) {
+        return rsrc((const T *)p.B + ((st.b * L + (int64_t)st.c * Q) * G + st.g) * N, chunk_len(st.c) * GN2);
     };
-    auto c_rows = [&](int64_t it, int c) {
-        return rsrc((const T *)p.C + ((seq_of(it) * L + (int64_t)c * Q) * G + group_of(it)) * N, chunk_len(c) * GN2);
+    auto c_rows = [&](const Step &st) {
+        return rsrc((const T *)p.C + ((st.b * L + (int64_t)st.c * Q) * G + st.g) * N, chunk_len(st.c) * GN2);
     };
 
     // ---- per-lane offsets, fixed for the whole loop.
@@ -212,19 +216,19 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     V8 xr[UXR], br[UBR];
     Frag<T> cf[KS];  // C rows of the wave's tile (phase A and blue)
     auto load_x = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = x_rows(st.item, st.c);
+        const auto r = x_rows(st);
 #pragma unroll
         for (int u = 0; u < UXR; ++u)
             xr[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vx, u * RX * HP2, 0));
     };
     auto load_b = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = b_rows(st.item, st.c);
+        const auto r = b_rows(st);
 #pragma unroll
         for (int u = 0; u < UBR; ++u)
             br[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vb, u * RB * GN2, 0));
     };
     auto load_c = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = c_rows(st.item, st.c);
+        const auto r = c_rows(st);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc + 64 * ks, 0, 0));
@@ -296,8 +300,8 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     };
     // The (b, h) state handed from a first half to a second half: entry
     // [b, 0, h] of the workspace's chunk-state region, and its flag.
-    auto handoff_rsrc = [&](int64_t it) {
-        return buffer_rsrc(p.states + ((seq_of(it) * nc) * H + head_of(it)) * (int64_t)P * N, (uint32_t)(P * N * 4));
+    auto handoff_rsrc = [&](const Step &st) {
+        return buffer_rsrc(p.states + ((st.b * nc) * H + st.h) * (int64_t)P * N, (uint32_t)(P * N * 4));
     };
     int *handoff_flag = p.sync + kSyncHeader;
     bool gave_up = false;  // a hand-off wait timed out (the wave waits no more)
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                 gave_up = true;
                 set_flag_device(p.sync + 1, 1);
             }
-            const auto r = handoff_rsrc(st.item);
+            const auto r = handoff_rsrc(st);
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                         *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
             }
         } else {
-            const auto r = handoff_rsrc(st.item);
+            const auto r = handoff_rsrc(st);
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -352,13 +356,13 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     };
     // Chunk whose entering state goes to hj (state_out at an index of -1 asks
     // for the initial state, which enters chunk 0), and the skip weight.
-    auto cj_of = [&](int64_t it) {
+    auto cj_of = [&](const Step &st) {
         if (!(p.hj && p.state_out_idx)) return -1;
-        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[seq_of(it)];
+        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[st.b];
         return j < 0 ? 0 : (int)(min((int64_t)j, L - 1) / Q);
     };
-    auto dh_of = [&](int64_t it) {
-        return p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[head_of(it)] : 0.f;
+    auto dh_of = [&](const Step &st) {
+        return p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[st.h] : 0.f;
     };
 
     // ---- per-chunk block factors (uniform).
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                         V4{(T)hs[a][q][0], (T)hs[a][q][1], (T)hs[a][q][2], (T)hs[a][q][3]};
                 }
         }
-        if (c == cj_of(st.item)) {
+        if (c == cj_of(st)) {
             uint32_t so[NTW][PTW];
             state_offsets(so);
             const int64_t hst = st.item * (int64_t)P * N;
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     // One chunk (tables in tb): blue, orange and D skip, stored; then the state.
     auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb) __attribute__((always_inline)) {
         const int c = st.c;
-        const float dh = dh_of(st.item);
+        const float dh = dh_of(st);
         const float cs2i = tb[16 * tile + il] * kLog2e;
         f32x4 acc[PT];
 #pragma unroll
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         }
         // y, rounded; rows past the sequence fall outside the buffer.
         if (live) {
-            const auto r = y_rows(st.item, c);
+            const auto r = y_rows(st);
 #pragma unroll
             for (int q = 0; q < PT; ++q) {
                 const V4 o = V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]};
