@@ -460,7 +460,8 @@ def main():
             work2 = algorithmic_work(w2, inp2.state_out_idx)
             workloads[name] = {"ms_per_step": round(m2, 5), "tokens_per_s": round(w2.tokens / (m2 * 1e-3), 1),
                                "TFLOP/s": round(total_flops(w2) / (m2 * 1e-3) / 1e12, 2),
-                               "alg_GB/s": round(sum(v["bytes"] for v in work2.values()) / (m2 * 1e-3) / 1e9, 1),
+                               "alg_GB/s": round(sum(work2[k]["bytes"] for k in r2["kernel_ms"]) / (m2 * 1e-3) / 1e9,
+                                                 1),
                                "kernel_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
             del inp2
 

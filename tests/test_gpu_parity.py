@@ -323,6 +323,9 @@ FUSED = [
     # Work split over a persistent grid of one workgroup per CU (256 here):
     (2, 300, 200, 64, 64, 1, 128, True, True, True),     # 400 pairs: 144 left over, too many to split
     (3, 700, 96, 64, 128, 1, 256, True, True, True),     # 288 pairs: 32 split in halves of 3 chunks (1 + 2)
+    # Many groups: every group's B and C rows are read by few heads.
+    (2, 600, 128, 64, 128, 64, 256, True, True, True),   # 2 heads per group
+    (2, 700, 128, 32, 64, 32, 128, True, True, True),    # 4 heads per group, 32 groups
 ]
 
 
