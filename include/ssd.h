@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -111,14 +111,15 @@ typedef struct {
  *            init_state is given (otherwise it is zero and left unwritten).
  *   hj       fp32 [batch, nheads, headdim, dstate]: the state entering the
  *            chunk that holds state_out_idx[b] (written only with state_out).
- *   sync     int32 [2 + batch*nheads]: a time-out word (nonzero if a wait of
+ *   sync     int32 [2 + 2*batch*nheads]: a time-out word (nonzero if a wait of
  *            the single-pass kernel for a state handed over by another
  *            workgroup gave up, which only a fault elsewhere can cause;
- *            outputs are then unspecified) and one hand-off flag per (b, h);
- *            cleared by the first kernel of each call.  The single-pass
- *            kernel hands a state over through the states region (entry
- *            [b, 0, h]) when it splits a sequence's chunks between two
- *            workgroups. */
+ *            outputs are then unspecified) and two hand-off flags per
+ *            (b, h) (one per half of the channels when headdim 128 is
+ *            split in two); cleared by the first kernel of each call.  The
+ *            single-pass kernel hands a state over through the states region
+ *            (entry [b, 0, h], the half's rows) when it splits a sequence's
+ *            chunks between two workgroups. */
 typedef struct {
     size_t cumsum_offset;
     size_t ct_offset;

@@ -75,7 +75,8 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
     // Clear the single-pass kernel's hand-off flag of (b, h) and the time-out
     // word for the kernel that follows.
     if (p.sync && c == 0 && lane == 0) {
-        p.sync[kSyncHeader + b * H + h] = 0;
+#pragma unroll
+        for (int f = 0; f < kFlagsPerHead; ++f) p.sync[kSyncHeader + (b * H + h) * kFlagsPerHead + f] = 0;
         if (b == 0 && h == 0) p.sync[1] = 0;
     }
 

@@ -1,5 +1,5 @@
-// Single-pass SSD forward (bf16): one workgroup per (sequence b, head h)
-// walks the chunks in order and keeps the running state in registers, so all
+// Single-pass SSD forward (bf16): one workgroup at a time per (sequence b,
+// head h) walks the chunks in order and keeps the running state in registers, so all
 // four parts of the block decomposition of "Transformers are SSMs"
 // (cloud.tencent.com.cn, section "SSD算法") run in one kernel: the chunk
 // states and the states entering each chunk never reach memory, x is read
@@ -30,6 +30,11 @@
 // on raw x (the mask applied through the exponent), so it stays exact
 // however strong the decay inside a block; the skip term D x_i enters as D
 // added to its j = i coefficient before rounding.
+//
+// Channels: the rows p of the state are independent (each is its own
+// recurrence), so a head of headdim 128 is run as two items of 64 channels
+// each, which share dt, B and C and own their columns of x and y and their
+// rows of the state.
 //
 // Work split: NIT = Q/16 waves, each owning one 16-row tile (balanced so
 // that every SIMD meets the same number of causal blocks) and, for the
@@ -115,10 +120,11 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     __shared__ __align__(16) float tb0[4 * 256], tb1[4 * 256];
 
     const int H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
+    const int PF = p.headdim, PS = PF / P;  // channels of a head, items per head
     const int64_t L = p.seqlen;
 
     // ---- work of this workgroup (one per CU, persistent).  A unit is the
-    // chunks [cb, ce) of one (b, h) pair ("item" b*H + h).  Workgroups are
+    // chunks [cb, ce) of one item, (b, h, channel half s): item (b*H + h)*PS + s.  Workgroups are
     // dealt to the XCDs in turn (w % 8), and each XCD takes a contiguous
     // range of items, so that the heads sharing B and C rows run on one
     // XCD and share its L2.  Within an XCD, with Ix items on Wx workgroups,
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int Wg = gridDim.x;
     const int NX = Wg % kXcds == 0 ? kXcds : 1;
     const int xcd = (int)blockIdx.x % NX, w = (int)blockIdx.x / NX, Wx = Wg / NX;
-    const int64_t I = p.batch * H;
+    const int64_t I = p.batch * H * PS;
     const int64_t Ibase = I / NX, Iext = I % NX;
     const int64_t Ix = Ibase + (xcd < Iext ? 1 : 0);
     const int64_t ibeg = xcd * Ibase + min((int64_t)xcd, Iext);  // first item of this XCD
@@ -159,13 +165,14 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         int k, c;
         int64_t item;
         int cb, ce;
-        int64_t b;
-        int h, g;
+        int64_t b, bh;  // bh = b*H + h
+        int h, g, s;
     };
     auto step_of = [&](int k, int c) -> Step {
         const Unit u = unit(k);
-        const uint32_t it = (uint32_t)u.item, hh = it % (uint32_t)H;
-        return Step{k, c, u.item, u.cb, u.ce, (int64_t)(it / (uint32_t)H), (int)hh, (int)hh / HPG};
+        const uint32_t it = (uint32_t)u.item, bh = it / (uint32_t)PS, hh = bh % (uint32_t)H;
+        return Step{k,           c,        u.item,  u.cb, u.ce, (int64_t)(bh / (uint32_t)H), (int64_t)bh,
+                    (int)hh,     (int)hh / HPG, (int)(it - bh * (uint32_t)PS)};
     };
     auto next_step = [&](const Step &st) -> Step {
         if (st.c + 1 < st.ce) {
@@ -184,14 +191,16 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int tile = wide_tile<NIT>(wave), md = tile >> 1;
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
-    const uint32_t HP2 = (uint32_t)H * P * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
+    const uint32_t HP2 = (uint32_t)H * PF * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
     auto chunk_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
     // Token rows of a step's chunk: x and y of its head, B and C of its group.
     auto x_rows = [&](const Step &st) {
-        return rsrc((const T *)p.x + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * P, chunk_len(st.c) * HP2);
+        return rsrc((const T *)p.x + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
+                    chunk_len(st.c) * HP2);
     };
     auto y_rows = [&](const Step &st) {
-        return rsrc((const T *)p.y + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * P, chunk_len(st.c) * HP2);
+        return rsrc((const T *)p.y + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
+                    chunk_len(st.c) * HP2);
     };
     auto b_rows = [&](const Step &st) {
         return rsrc((const T *)p.B + ((st.b * L + (int64_t)st.c * Q) * G + st.g) * N, chunk_len(st.c) * GN2);
@@ -237,14 +246,14 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     // block factors (64 bytes, wave 3; its other lanes repeat the last piece).
     static_assert(Cf::W >= 4, "four waves copy the tables");
     auto issue_tables = [&](const Step &st, float *dst) __attribute__((always_inline)) {
-        const int64_t row = (st.item * nc + st.c) * (int64_t)Q;  // tables are [b,H,nc,Q]: item-major
+        const int64_t row = (st.bh * nc + st.c) * (int64_t)Q;  // tables are [b,H,nc,Q]
         int ln = lane;
         asm volatile("" : "+v"(ln));
         if (wave < 3)
             copy16_to_lds((wave == 0 ? p.cs : wave == 1 ? p.ct : p.dte) + row + 4 * min(ln, Q / 4 - 1),
                           dst + 256 * wave);
         else if (wave == 3)
-            copy16_to_lds(p.blk + (st.item * nc + st.c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
+            copy16_to_lds(p.blk + (st.bh * nc + st.c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
                           dst + 768);
     };
 
@@ -298,18 +307,20 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
             for (int q = 0; q < PTW; ++q)
                 so[a][q] = (uint32_t)((16 * (pw * PTW + q) + (ln & 15)) * N + 16 * (nw * NTW + a) + 4 * (ln >> 4));
     };
-    // The (b, h) state handed from a first half to a second half: entry
-    // [b, 0, h] of the workspace's chunk-state region, and its flag.
+    // The item's state handed from a first half to a second half: its rows
+    // of entry [b, 0, h] of the workspace's chunk-state region, and its flag.
     auto handoff_rsrc = [&](const Step &st) {
-        return buffer_rsrc(p.states + ((st.b * nc) * H + st.h) * (int64_t)P * N, (uint32_t)(P * N * 4));
+        return buffer_rsrc(p.states + (((st.b * nc) * H + st.h) * PF + st.s * P) * (int64_t)N, (uint32_t)(P * N * 4));
     };
     int *handoff_flag = p.sync + kSyncHeader;
+    auto flag_of = [&](const Step &st) { return st.bh * kFlagsPerHead + st.s; };
     bool gave_up = false;  // a hand-off wait timed out (the wave waits no more)
     // Start a unit: h_{cb-1} is the initial state (or 0) for cb = 0, else
     // the state the first half handed over.
     auto begin_unit = [&](const Step &st) __attribute__((always_inline)) {
         uint32_t so[NTW][PTW];
         state_offsets(so);
+        // item * P * N = (bh * PF + s * P) * N: the item's rows of its head's state
         const int64_t hst = st.item * (int64_t)P * N;
         if (st.cb == 0) {
 #pragma unroll
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                     hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
                                             : f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
-            if (!gave_up && !wait_flag_device(handoff_flag + st.item, kSpinLimit)) {
+            if (!gave_up && !wait_flag_device(handoff_flag + flag_of(st), kSpinLimit)) {
                 gave_up = true;
                 set_flag_device(p.sync + 1, 1);
             }
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                 for (int q = 0; q < PTW; ++q) store_f4_device(r, 4 * so[a][q], hs[a][q]);
             wait_vmcnt<0>();  // every store of this wave is visible device-wide ...
             barrier_only();   // ... and of every wave
-            if (wave == 0) set_flag_device(handoff_flag + st.item, 1);
+            if (wave == 0) set_flag_device(handoff_flag + flag_of(st), 1);
         }
     };
     // Chunk whose entering state goes to hj (state_out at an index of -1 asks
@@ -593,7 +604,7 @@ hipError_t launch_cfg(const Params &p, hipStream_t stream) {
         return hipErrorNotSupported;
     } else {
         // One workgroup per CU (each takes one CU's LDS); never more than items.
-        const int64_t items = p.batch * p.nheads;
+        const int64_t items = p.batch * p.nheads * (p.headdim / Cf::P);
         const int64_t grid = std::min<int64_t>(items, compute_units());
         hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, NIT>), dim3((unsigned)grid), dim3(Cf::THREADS), 0,
                            stream, p);
@@ -615,6 +626,7 @@ hipError_t dispatch_p(const Params &p, hipStream_t stream) {
     switch (p.headdim) {
         case 32: return dispatch_q<NT, 2>(p, stream);
         case 64: return dispatch_q<NT, 4>(p, stream);
+        case 128: return dispatch_q<NT, 4>(p, stream);  // two 64-channel items per head
         default: return hipErrorNotSupported;
     }
 }
@@ -622,9 +634,9 @@ hipError_t dispatch_p(const Params &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream) {
-    // One workgroup per (b, h) and one CU each: with fewer than a CU's worth
+    // One workgroup per item and one CU each: with fewer than a CU's worth
     // of them the chunk-parallel kernels use the GPU better.
-    if (p.batch * p.nheads < kFusedMinHeads) return hipErrorNotSupported;
+    if (p.batch * p.nheads * (p.headdim == 128 ? 2 : 1) < kFusedMinHeads) return hipErrorNotSupported;
     switch (p.dstate) {
         case 64: return dispatch_p<4>(p, stream);
         case 128: return dispatch_p<8>(p, stream);

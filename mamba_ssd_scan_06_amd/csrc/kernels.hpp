@@ -11,7 +11,10 @@ enum class Elem { F32, BF16 };
 
 constexpr int kBlkStride = 16;  // floats per (b, h, c) in the block-factor table
 constexpr int kSyncHeader = 2;  // words before the hand-off flags in the sync region
-inline int64_t sync_words(int64_t batch, int64_t nheads) { return kSyncHeader + batch * nheads; }
+// The single-pass kernel may split a head's channels p in two (headdim 128:
+// two independent 64-channel halves), so each (b, h) has two flags.
+constexpr int kFlagsPerHead = 2;
+inline int64_t sync_words(int64_t batch, int64_t nheads) { return kSyncHeader + kFlagsPerHead * batch * nheads; }
 
 // Everything a kernel needs, passed by value.  Pointers are device pointers
 // with the layouts documented in include/ssd.h; `cs` and `states` point into
@@ -56,10 +59,12 @@ hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // shape does not fit its LDS budget (the caller then uses launch_chunk_output).
 hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_at_index(const Params &p, Elem e, hipStream_t stream);
-// Single-pass bf16 forward: one workgroup per (b, h) runs every chunk in
-// order with the state in registers (after launch_chunk_cumsum; writes y,
-// final_state and, with state_out, hj).  Returns hipErrorNotSupported for
-// shapes it does not take or with fewer than kFusedMinHeads (b, h) pairs.
+// Single-pass bf16 forward: a persistent grid in which one workgroup at a
+// time runs every chunk of an item ((b, h), or a 64-channel half of a head of
+// headdim 128) in order with the state in registers (after
+// launch_chunk_cumsum; writes y, final_state and, with state_out, hj).
+// Returns hipErrorNotSupported for shapes it does not take or with fewer
+// than kFusedMinHeads items.
 constexpr int64_t kFusedMinHeads = 256;
 hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream);
 // Whole forward of a one-chunk call of at most 32 tokens in one kernel (y,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ssd.ssd_abi_version() == 4
+    assert ssd.ssd_abi_version() == 5
 
 
 def test_status_strings():
@@ -54,7 +54,7 @@ def test_workspace_bytes_formula():
     n_st = 2 * nc * 4 * 64 * 128             # states, prev: [b,nc,H,P,N]
     n_hj = 2 * 4 * 64 * 128                  # hj: [b,H,P,N]
     n_blk = 2 * 4 * nc * 16                  # block_decay: [b,H,nc,16]
-    n_sync = 2 + 2 * 4                       # sync: time-out word + header, one flag per (b, h)
+    n_sync = 2 + 2 * 2 * 4                   # sync: time-out word + header, two flags per (b, h)
     rnd = lambda v: (v + 255) // 256 * 256
     lay = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_BF16)
     assert lay.nchunks == nc and lay.cumsum_offset == 0

@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 4
+    assert ssd.ssd_abi_version() == 5
 
 
 # ----------------------------------------------------------- full workloads
@@ -326,6 +326,9 @@ FUSED = [
     # Many groups: every group's B and C rows are read by few heads.
     (2, 600, 128, 64, 128, 64, 256, True, True, True),   # 2 heads per group
     (2, 700, 128, 32, 64, 32, 128, True, True, True),    # 4 heads per group, 32 groups
+    # headdim 128: each head runs as two 64-channel items
+    (2, 700, 64, 128, 128, 8, 128, True, True, True),    # 256 items
+    (3, 600, 48, 128, 64, 4, 256, True, True, True),     # 288 items: 32 split in chunk halves
 ]
 
 
