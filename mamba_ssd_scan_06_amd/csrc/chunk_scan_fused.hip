@@ -56,6 +56,7 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kStep = 32;  // tokens per j block
 constexpr int kSpinLimit = 1 << 20;  // polls before a hand-off wait gives up (well over 0.1 s)
+constexpr int kAuxNt = 2;  // cache-policy operand of the buffer builtins: nt (non-temporal)
 
 // Compute units of the current device (cached per device).
 int compute_units() {
@@ -520,13 +521,35 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < PT; ++q) mma(read_tr(xs + kStep * md * P, xo[q], P), lf, acc[q]);
         }
-        // y, rounded; rows past the sequence fall outside the buffer.
+        // y, rounded; rows past the sequence fall outside the buffer.  y is
+        // written once and not read here: non-temporal stores (kAuxNt) keep
+        // it from displacing the B and C rows the other heads still read.
+        // Lane (il, grp) holds channels 16q + 4grp .. +3 of row il; the four
+        // lanes of a row swap values so that lane g holds channels
+        // 32k + 8g .. +7 for k < PT/2 and each store writes 64 contiguous
+        // bytes of every row (whole 64-byte pieces, no partial writes).
         if (live) {
             const auto r = y_rows(st);
+            int ln = lane;  // opaque: the shuffle sources are recomputed here
+            asm volatile("" : "+v"(ln));
+            const int g = ln >> 4, s0 = ((ln & 15) + 32 * (g & 1)) << 2, s1 = s0 + 64;
+            u32x2 o[PT];
 #pragma unroll
-            for (int q = 0; q < PT; ++q) {
-                const V4 o = V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]};
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), r, vy + 32 * q, 0, 0);
+            for (int q = 0; q < PT; ++q)
+                o[q] = __builtin_bit_cast(u32x2, V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]});
+            const uint32_t vyr = (uint32_t)(16 * tile + (ln & 15)) * HP2 + 16 * g;
+#pragma unroll
+            for (int k = 0; k < PT / 2; ++k) {
+                u32x4 w[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {  // channels 16(2k + j) + 4grp' .., grp' = 2(g & 1) and 2(g & 1) + 1
+                    const u32x2 v = o[2 * k + j];
+                    w[j] = u32x4{(unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[0]),
+                                 (unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[1]),
+                                 (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[0]),
+                                 (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[1])};
+                }
+                __builtin_amdgcn_raw_buffer_store_b128((g >> 1) ? w[1] : w[0], r, vyr + 64 * k, 0, kAuxNt);
             }
         }
         // C rows of the next chunk (cf is no longer needed).

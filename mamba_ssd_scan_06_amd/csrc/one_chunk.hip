@@ -120,11 +120,25 @@ __global__ __launch_bounds__(kThreads) void one_chunk_kernel(Params p) {
     T *yg = reinterpret_cast<T *>(p.y);
     const int64_t hbase = (b * H + h) * (int64_t)P * N;
 
-    for (int pass = 0; pass < P / RPP; ++pass) {
+    // The initial-state rows of up to kInFlight passes are requested before
+    // any of their results is stored: a wave's loads and stores complete in
+    // order, so a load issued after a store would also wait for that store.
+    constexpr int NPASS = P / RPP;
+    constexpr int kInFlight = NPASS < 16 ? NPASS : 16;
+    static_assert(NPASS % kInFlight == 0, "pass groups");
+    f32x4 h0s[kInFlight];
+    for (int g0 = 0; g0 < NPASS; g0 += kInFlight) {
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i)
+          h0s[i] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hbase +
+                                                                    (int64_t)((g0 + i) * RPP + rg) * N + n0)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i) {
+        const int pass = g0 + i;
         const int pp = pass * RPP + rg;
         const int64_t at = hbase + (int64_t)pp * N + n0;
-        const f32x4 h0 = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + at)
-                                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 h0 = h0s[i];
         f32x4 fin = eT * h0, sout = ej * h0;
         float v[MT];  // partial h0 . C_t over this lane's four columns
 #pragma unroll
@@ -139,8 +153,10 @@ __global__ __launch_bounds__(kThreads) void one_chunk_kernel(Params p) {
                 v[s] = cv[0] * h0[0] + cv[1] * h0[1] + cv[2] * h0[2] + cv[3] * h0[3];
             }
         }
-        if (p.final_state) *reinterpret_cast<f32x4 *>(p.final_state + at) = fin;
-        if (p.state_out) *reinterpret_cast<f32x4 *>(p.state_out + at) = sout;
+        // Both states are written once and not read again here: non-temporal
+        // stores keep them from displacing lines that are still to be read.
+        if (p.final_state) __builtin_nontemporal_store(fin, reinterpret_cast<f32x4 *>(p.final_state + at));
+        if (p.state_out) __builtin_nontemporal_store(sout, reinterpret_cast<f32x4 *>(p.state_out + at));
 
         // Sum v over the TPR lanes of the row by reduce-scatter: each step
         // on lane bit d halves the values a lane holds (keeping the upper or
@@ -177,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void one_chunk_kernel(Params p) {
                 }
             }
         }
+      }
     }
 }
 
