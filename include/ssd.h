@@ -91,7 +91,13 @@ typedef struct {
 /* Where the intermediates live inside the workspace after a call (byte
  * offsets from the workspace pointer).  Exposed so that the individual steps
  * can be checked.  A call whose tokens fit one chunk and number at most 32
- * is computed by one fused kernel and leaves the workspace untouched.
+ * is computed by one fused kernel and leaves the workspace untouched.  bf16
+ * calls with dstate 64 or 128, headdim 32, 64 or 128, chunk_size 128 or 256
+ * and at least 256 items (an item is a (b, h) pair, or a 64-channel half of
+ * a head of headdim 128) run the single-pass kernel after the cumsum: it
+ * fills cumsum, ct, dt_decay, block_decay, hj and sync, uses only hand-off
+ * entries of states and leaves prev unwritten.  Every other call runs the
+ * chunk-parallel kernels, which fill every region but sync.
  *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
  *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
  *            past seqlen count as dt = 0.
