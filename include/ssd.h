@@ -95,9 +95,10 @@ typedef struct {
  * calls with dstate 64 or 128, headdim 32, 64 or 128, chunk_size 128 or 256
  * and at least 256 items (an item is a (b, h) pair, or a 64-channel half of
  * a head of headdim 128) run the single-pass kernel after the cumsum: it
- * fills cumsum, ct, dt_decay, block_decay, hj and sync, uses only hand-off
- * entries of states and leaves prev unwritten.  Every other call runs the
- * chunk-parallel kernels, which fill every region but sync.
+ * fills cumsum, ct, dt_decay, block_decay, sync and (with state_out) hj,
+ * uses only hand-off entries of states and leaves prev unwritten.  Every
+ * other call runs the chunk-parallel kernels, which fill every region (sync
+ * is only cleared).
  *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
  *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
  *            past seqlen count as dt = 0.
