@@ -191,9 +191,15 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
     const int il = lane & 15, grp = lane >> 4;
     const int tile = wide_tile<NIT>(wave), md = tile >> 1;
     // Waves meet md off-diagonal blocks each, so the chunk lasts as long as
-    // the waves with the most; those get the higher issue priority, the
+    // the waves with the most; issue priority grows with md (0 .. 3), so the
     // others fill the gaps (a SIMD's four waves together meet the same number).
-    if (md >= NBLK / 2) __builtin_amdgcn_s_setprio(3);
+    const int prio = md * 4 / NBLK;
+    if (prio >= 3)
+        __builtin_amdgcn_s_setprio(3);
+    else if (prio == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else if (prio == 1)
+        __builtin_amdgcn_s_setprio(1);
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
     const uint32_t HP2 = (uint32_t)H * PF * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
