@@ -329,6 +329,7 @@ FUSED = [
     # headdim 128: each head runs as two 64-channel items
     (2, 700, 64, 128, 128, 8, 128, True, True, True),    # 256 items
     (3, 600, 48, 128, 64, 4, 256, True, True, True),     # 288 items: 32 split in chunk halves
+    (2, 450, 128, 128, 64, 128, 128, False, True, False),  # 512 items, one head per group, zero start, no D
 ]
 
 
