@@ -129,71 +129,71 @@ __global__ __launch_bounds__(kThreads) void one_chunk_kernel(Params p) {
     f32x4 h0s[kInFlight];
     for (int g0 = 0; g0 < NPASS; g0 += kInFlight) {
 #pragma unroll
-      for (int i = 0; i < kInFlight; ++i)
-          h0s[i] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hbase +
-                                                                    (int64_t)((g0 + i) * RPP + rg) * N + n0)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kInFlight; ++u)
+            h0s[u] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hbase +
+                                                                      (int64_t)((g0 + u) * RPP + rg) * N + n0)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < kInFlight; ++i) {
-        const int pass = g0 + i;
-        const int pp = pass * RPP + rg;
-        const int64_t at = hbase + (int64_t)pp * N + n0;
-        const f32x4 h0 = h0s[i];
-        f32x4 fin = eT * h0, sout = ej * h0;
-        float v[MT];  // partial h0 . C_t over this lane's four columns
+        for (int u = 0; u < kInFlight; ++u) {
+            const int pass = g0 + u;
+            const int pp = pass * RPP + rg;
+            const int64_t at = hbase + (int64_t)pp * N + n0;
+            const f32x4 h0 = h0s[u];
+            f32x4 fin = eT * h0, sout = ej * h0;
+            float v[MT];  // partial h0 . C_t over this lane's four columns
 #pragma unroll
-        for (int s = 0; s < MT; ++s) {
-            v[s] = 0.f;
-            if (s < L) {
-                const float xv = xs[s][pp];
-                const f32x4 bv = *reinterpret_cast<const f32x4 *>(&bsh[s][n0]);
-                fin += (wsh[L - 1][s] * xv) * bv;
-                if (s <= j) sout += (wsh[j][s] * xv) * bv;
-                const f32x4 cv = *reinterpret_cast<const f32x4 *>(&csh[s][n0]);
-                v[s] = cv[0] * h0[0] + cv[1] * h0[1] + cv[2] * h0[2] + cv[3] * h0[3];
+            for (int s = 0; s < MT; ++s) {
+                v[s] = 0.f;
+                if (s < L) {
+                    const float xv = xs[s][pp];
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&bsh[s][n0]);
+                    fin += (wsh[L - 1][s] * xv) * bv;
+                    if (s <= j) sout += (wsh[j][s] * xv) * bv;
+                    const f32x4 cv = *reinterpret_cast<const f32x4 *>(&csh[s][n0]);
+                    v[s] = cv[0] * h0[0] + cv[1] * h0[1] + cv[2] * h0[2] + cv[3] * h0[3];
+                }
             }
-        }
-        // Both states are written once and not read again here: non-temporal
-        // stores keep them from displacing lines that are still to be read.
-        if (p.final_state) __builtin_nontemporal_store(fin, reinterpret_cast<f32x4 *>(p.final_state + at));
-        if (p.state_out) __builtin_nontemporal_store(sout, reinterpret_cast<f32x4 *>(p.state_out + at));
+            // Both states are written once and not read again here: non-temporal
+            // stores keep them from displacing lines that are still to be read.
+            if (p.final_state) __builtin_nontemporal_store(fin, reinterpret_cast<f32x4 *>(p.final_state + at));
+            if (p.state_out) __builtin_nontemporal_store(sout, reinterpret_cast<f32x4 *>(p.state_out + at));
 
-        // Sum v over the TPR lanes of the row by reduce-scatter: each step
-        // on lane bit d halves the values a lane holds (keeping the upper or
-        // lower half of the t range by that bit), then plain sums.
-        int tbase = 0;
-        int len = MT;
-        static_for<kLog2Tpr>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int d = TPR >> (decltype(kc)::value + 1);
-            constexpr int half = MT >> (decltype(kc)::value + 1);
-            const bool upper = (lr & d) != 0;
-            if constexpr (half >= 1) {
+            // Sum v over the TPR lanes of the row by reduce-scatter: each step
+            // on lane bit d halves the values a lane holds (keeping the upper or
+            // lower half of the t range by that bit), then plain sums.
+            int tbase = 0;
+            int len = MT;
+            static_for<kLog2Tpr>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int d = TPR >> (decltype(kc)::value + 1);
+                constexpr int half = MT >> (decltype(kc)::value + 1);
+                const bool upper = (lr & d) != 0;
+                if constexpr (half >= 1) {
 #pragma unroll
-                for (int i = 0; i < half; ++i) {
-                    const float send = upper ? v[i] : v[half + i];
-                    const float keep = upper ? v[half + i] : v[i];
-                    v[i] = keep + __shfl_xor(send, d, 64);
+                    for (int i = 0; i < half; ++i) {
+                        const float send = upper ? v[i] : v[half + i];
+                        const float keep = upper ? v[half + i] : v[i];
+                        v[i] = keep + __shfl_xor(send, d, 64);
+                    }
+                    if (upper) tbase += half;
+                } else {
+                    v[0] += __shfl_xor(v[0], d, 64);
                 }
-                if (upper) tbase += half;
-            } else {
-                v[0] += __shfl_xor(v[0], d, 64);
-            }
-        });
-        (void)len;
-        // The lane now holds (h0 C_t)[pp] for t = tbase .. tbase + KEEP - 1;
-        // the lanes with the low bits clear write y_t[pp].
-        if ((lr & (TPR / (MT < TPR ? MT : TPR) - 1)) == 0 || MT >= TPR) {
+            });
+            (void)len;
+            // The lane now holds (h0 C_t)[pp] for t = tbase .. tbase + KEEP - 1;
+            // the lanes with the low bits clear write y_t[pp].
+            if ((lr & (TPR / (MT < TPR ? MT : TPR) - 1)) == 0 || MT >= TPR) {
 #pragma unroll
-            for (int i = 0; i < KEEP; ++i) {
-                const int t = tbase + i;
-                if (t < L) {
-                    float yv = esh[t] * v[i] + dh * xs[t][pp];
-                    for (int s2 = 0; s2 <= t; ++s2) yv += msh[t][s2] * xs[s2][pp];
-                    yg[((b * L + t) * H + h) * P + pp] = (T)yv;
+                for (int i = 0; i < KEEP; ++i) {
+                    const int t = tbase + i;
+                    if (t < L) {
+                        float yv = esh[t] * v[i] + dh * xs[t][pp];
+                        for (int s2 = 0; s2 <= t; ++s2) yv += msh[t][s2] * xs[s2][pp];
+                        yg[((b * L + t) * H + h) * P + pp] = (T)yv;
+                    }
                 }
             }
         }
-      }
     }
 }
 
