@@ -1,52 +1,71 @@
-// Single-pass SSD forward (bf16): one workgroup at a time per (sequence b,
-// head h) walks the chunks in order and keeps the running state in registers, so all
-// four parts of the block decomposition of "Transformers are SSMs"
+// Single-pass SSD forward (bf16): one workgroup at a time per item (sequence
+// b, head h, or a 64-channel half of a head of headdim 128) walks the
+// sequence in blocks of 128 tokens and keeps the running state in registers,
+// so all four parts of the block decomposition of "Transformers are SSMs"
 // (cloud.tencent.com.cn, section "SSD算法") run in one kernel: the chunk
-// states and the states entering each chunk never reach memory, x is read
+// states and the states entering each block never reach memory, x is read
 // once and y written once.  The state passing is the sequential scan over
-// chunks that section "深入解析分块与状态传递机制" describes, here carried
-// by the workgroup itself.
+// chunks of section "深入解析分块与状态传递机制", carried by the workgroup.
+// The chunk-local cumulative decay is computed here too (from dt and A), so
+// the call is this one kernel.
 //
-// Chunk c (tokens t0 .. t0+Qc-1, head h of group g), with cs the chunk-local
-// cumulative log-decay, cs2 = cs log2(e), ct = cs2 - log2(dt), e(m) the last
-// token of 32-token block m and dte_j = dt_j exp(cs_e(m) - cs_j) for j in m
-// (the tables of the cumsum kernel, which also gives cs2_e(m) and the
-// state's Horner factors per block):
-//   G      = C_c B_c^T (causal 16x32 tiles, bf16, nearest even)
+// The kernel's block length (128 tokens) is its own and does not depend on
+// the chunk_size of the call: every block length gives the same result up
+// to rounding, since the block decomposition is an exact re-association.
+//
+// Block c (tokens t0 .. t0+Qc-1), head h of group g; cs the block-local
+// inclusive cumulative log-decay A_h sum dt, cs2 = cs log2(e),
+// ct_j = cs2_j - log2(dt_j), e(m) the last token of 32-token block m and
+// dte_j = dt_j exp(cs_e(m) - cs_j) for j in m (all computed per block by one
+// wave, in fp64 and rounded once):
+//   G      = C B^T (causal 16x32 tiles, fp32 accumulate)
 //   orange y_i  = sum_{j<=i} exp(cs_i - cs_j) dt_j G_ij x_j
 //   blue   y_i += exp(cs_i) C_i . h_{c-1}
 //   green  h_c  = exp(cs_last) h_{c-1} + sum_j exp(cs_last - cs_j) dt_j x_j B_j^T
 //          y_i += D_h x_i.
-// Decay factors.  Outside the diagonal blocks every factor splits into the
-// per-token dte_j, applied once to x (xd = dte x, rounded to bf16), and
-// factors of at most 1 that depend on the block only:
-//   orange, block m < md (md the tile's diagonal block): G_ij times
-//     exp2(cs2_i - cs2_e(m)), rounded to bf16, on xd;
+// Decay factors.  Every factor applied is at most max(1, dt):
+//   orange, block m below the tile's diagonal block md: G_ij times
+//     exp2(cs2_i - cs2_e(m)) dte_j, rounded once to bf16, on raw x;
+//   orange, diagonal block md: G_ij times the exact exp2(cs2_i - ct_j)
+//     (selected to 0 above the diagonal), plus D at j = i, rounded
+//     once, on raw x; exact however strong the decay inside the block;
 //   blue: exp2(cs2_i) times C_i . h_{c-1};
-//   state, in Horner form: acc = h_{c-1}; acc = acc g_m + B_m^T xd_m over the
-//     chunk's blocks, g_0 = exp2(cs2_e(0)), g_m = exp2(cs2_e(m) - cs2_e(m-1)),
-//     which leaves h_c (e of the last block is the chunk's last token).
-// The diagonal block keeps the exact factor exp2(cs2_i - ct_j) per element
-// on raw x (the mask applied through the exponent), so it stays exact
-// however strong the decay inside a block; the skip term D x_i enters as D
-// added to its j = i coefficient before rounding.
+//   state, in Horner form over the 32-token blocks: acc = acc g_m +
+//     B_m^T (dte x)_m with g_0 = exp(cs_e(0)), g_m = exp(cs_e(m) - cs_e(m-1));
+//     dte x is formed from the transposed x fragment and rounded once.
+// The state after an accepted index j (multi-step verify, "3天把Llama训成
+// Mamba", blog.csdn.net, section "推测解码") is computed in the block holding
+// j, from the state entering it, with the exact factors exp2(cs2_j - ct_s):
+//   h_j = exp(cs_j) h_{c-1} + sum_{s<=j} exp(cs_j - cs_s) dt_s x_s B_s^T.
 //
-// Channels: the rows p of the state are independent (each is its own
-// recurrence), so a head of headdim 128 is run as two items of 64 channels
-// each, which share dt, B and C and own their columns of x and y and their
-// rows of the state.
+// Channels: the rows p of the state are independent recurrences, so a head
+// of headdim 128 runs as two items of 64 channels, which share dt, B and C
+// and own their columns of x and y and their rows of the state.
 //
-// Work split: NIT = Q/16 waves, each owning one 16-row tile (balanced so
-// that every SIMD meets the same number of causal blocks) and, for the
-// state, NTW x PTW of its 16x16 tiles.  LDS holds the chunk's B rows, x and
-// xd rows (token-major, read with the transposing LDS read) and h_{c-1} in
-// bf16.  While chunk c computes, chunk c+1's x and B rows are loaded into
-// registers and its tables copied to LDS; its C rows follow once chunk c no
-// longer needs them.  At the switch every wave waits for its loads and
-// writes the next chunk's LDS, and one barrier publishes them.  y is stored
-// before the state part, whose products cover the stores' latency.  Global
-// accesses go through buffer descriptors over each chunk's rows, with fixed
-// per-lane offsets.
+// Work split inside a workgroup: 8 waves, each owning one 16-row tile of
+// the block (tiles dealt so that both waves of a SIMD meet 3 off-diagonal
+// 32-token blocks together) and NTW x PTW 16x16 tiles of the state.  LDS
+// holds the block's B rows and x rows (token-major, read with the
+// transposing LDS read), h_{c-1} in bf16 and the per-token tables.  Under
+// 80 KB at dstate 128, so two workgroups share a compute unit and one's
+// block switch overlaps the other's products.  While block c computes,
+// block c+1's x and B rows are loaded into registers and its dt values
+// fetched (wave 0 turns them into block c+1's tables); its C rows follow
+// once block c no longer needs them.  At the switch every wave waits for
+// its loads and writes the next block's LDS, and one barrier publishes
+// them.  Global accesses go through buffer descriptors over each block's
+// rows (rows past the sequence read as zero, their stores are dropped).
+//
+// Schedule: a grid of two workgroups per compute unit; workgroup w runs on
+// XCD w mod 8 (the hardware deals workgroups to the XCDs in turn), and each
+// XCD takes a contiguous range of items, so heads sharing B and C rows share
+// that XCD's L2.  With at least as many items as workgroups, each takes
+// whole items and the leftovers are split in two halves of their blocks;
+// with fewer, every item is split in up to four ranges.  A range that does
+// not start at block 0 first runs the state recurrence alone (no C, no y)
+// over the blocks before it, from the initial state: recomputing is cheaper
+// than waiting for another workgroup, and no workgroup ever waits for
+// another one.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -54,9 +73,18 @@ namespace ssd {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kStep = 32;  // tokens per j block
-constexpr int kSpinLimit = 1 << 20;  // polls before a hand-off wait gives up (well over 0.1 s)
-constexpr int kAuxNt = 2;  // cache-policy operand of the buffer builtins: nt (non-temporal)
+constexpr int kQ = 128;             // tokens per block
+constexpr int kStep = 32;           // tokens per j block (one MFMA k step)
+constexpr int kNBlk = kQ / kStep;   // 32-token blocks per block
+constexpr int kWaves = 8;           // one 16-row tile per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxRanges = 4;       // ranges per item when items are fewer than workgroups
+constexpr int kAuxNt = 2;           // cache-policy operand of the buffer builtins: nt (non-temporal)
+constexpr double kLog2eD = 1.4426950408889634074;
+// Per-block tables in LDS (floats): cs2, ct, dte per token, then cs2 at the
+// end of each 32-token block and the Horner factors.
+constexpr int kTbCs2 = 0, kTbCt = kQ, kTbDte = 2 * kQ, kTbCe = 3 * kQ, kTbG = 3 * kQ + kNBlk;
+constexpr int kTbSize = 3 * kQ + 2 * kNBlk;
 
 // Compute units of the current device (cached per device).
 int compute_units() {
@@ -71,238 +99,319 @@ int compute_units() {
     return cached[dev];
 }
 
-template <int NT, int PT, int NIT>
+template <int NT, int PT>
 struct FusedCfg {
-    static constexpr int N = NT * 16, P = PT * 16, Q = NIT * 16;
-    static constexpr int W = NIT, THREADS = 64 * NIT;          // one 16-row tile per wave
-    static constexpr int KS = N / 32;                            // 32-wide k steps over n
-    static constexpr int WB = N / 8, WX = P / 8;                 // 16-byte pieces per B row, per x row
-    static constexpr int NBLK = Q / kStep;
-    static constexpr int WPN = NT < W ? NT : W, WPP = W / WPN;  // waves along n, p (state tiles)
-    static constexpr int NTW = NT / WPN, PTW = PT / WPP;         // state tiles per wave
-    static constexpr int UXR = Q * WX / THREADS;                 // 16-byte x pieces per thread
-    static constexpr int UBR = Q * WB / THREADS;                 // 16-byte B pieces per thread
-    static constexpr size_t LDS_BYTES =
-        (size_t)Q * N * 2 + 2 * (size_t)Q * P * 2 + (size_t)P * N * 2 + 2 * 4 * 256 * 4;
-    static constexpr bool OK = NIT >= 8 && NT >= 2 && NT % WPN == 0 && PT % WPP == 0 && PTW >= 1 &&
-                               (Q * WX) % THREADS == 0 && UXR >= 1 && (Q * WB) % THREADS == 0 &&
-                               LDS_BYTES <= 160 * 1024;
+    static constexpr int N = NT * 16, P = PT * 16, Q = kQ;
+    static constexpr int KS = N / 32;                 // 32-wide k steps over n
+    static constexpr int WB = N / 8, WX = P / 8;      // 16-byte pieces per B row, per x row
+    static constexpr int WPP = 2, WPN = kWaves / WPP; // waves along p, n (state tiles)
+    static constexpr int NTW = NT / WPN, PTW = PT / WPP;
+    static constexpr int UXR = Q * WX / kThreads;     // 16-byte x pieces per thread
+    static constexpr int UBR = Q * WB / kThreads;     // 16-byte B pieces per thread
+    // LDS rows are padded by 32 bytes: 16 lanes reading 16 bytes of 16
+    // consecutive rows, and the transposing reads of 4 consecutive rows,
+    // then spread over the banks, and every fragment address is one
+    // per-lane base plus an immediate offset.
+    static constexpr int SB = N * 2 + 32, SX = P * 2 + 32, SH = N * 2 + 32;  // bytes per LDS row of B, x, h
+    static constexpr size_t LDS_BYTES = (size_t)Q * SB + (size_t)Q * SX + (size_t)P * SH + 2 * kTbSize * 4;
+    static constexpr bool OK = NT % WPN == 0 && PT % WPP == 0 && NTW >= 1 && PTW >= 1 && UXR >= 1 && UBR >= 1 &&
+                               (Q * WX) % kThreads == 0 && (Q * WB) % kThreads == 0 && LDS_BYTES <= 80 * 1024;
+    static_assert(!OK || LDS_BYTES <= 81920, "two workgroups per compute unit");
 };
 
 // Raw buffer descriptor over [base, base + bytes): loads beyond it read 0
-// and stores beyond it are dropped, which takes care of rows past the end of
-// the sequence.  Word 3 selects 32-bit data, the gfx9 value for untyped access.
+// and stores beyond it are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <int NT, int PT, int NIT>
-__global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
-    using Cf = FusedCfg<NT, PT, NIT>;
+__device__ __forceinline__ double shfl_f64(double v, int src) {
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2loint(v));
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+// bf16 fragment times per-slot fp32 factors, rounded once to bf16.
+__device__ __forceinline__ void scale_frag(Frag<bf16> &f, const f32x4 &w0, const f32x4 &w1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        f.v[s] = (bf16)((float)f.v[s] * w0[s]);
+        f.v[4 + s] = (bf16)((float)f.v[4 + s] * w1[s]);
+    }
+}
+
+template <int NT, int PT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void chunk_scan_fused_kernel(Params p) {
+    using Cf = FusedCfg<NT, PT>;
     using T = bf16;
-    constexpr int N = Cf::N, P = Cf::P, Q = Cf::Q, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
-    constexpr int NBLK = Cf::NBLK, NTW = Cf::NTW, PTW = Cf::PTW, UXR = Cf::UXR, UBR = Cf::UBR;
-    constexpr int THREADS = Cf::THREADS;
-    constexpr int RX = THREADS / WX, RB = THREADS / WB;  // rows between a thread's x / B pieces
-    static_assert(RX % 8 == 0 && RB % 8 == 0, "a thread's pieces share one swizzle");
+    constexpr int N = Cf::N, P = Cf::P, Q = kQ, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
+    constexpr int NTW = Cf::NTW, PTW = Cf::PTW, UXR = Cf::UXR, UBR = Cf::UBR;
+    constexpr int SB = Cf::SB, SX = Cf::SX, SH = Cf::SH;
+    constexpr int RX = kThreads / WX, RB = kThreads / WB;  // rows between a thread's x / B pieces
     typedef typename Vec8<T>::type V8;
     typedef typename Vec4<T>::type V4;
     typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-    __shared__ __align__(16) T bl[Q * N];   // B rows, pieces swizzled for the transposing read
-    __shared__ __align__(16) T xs[Q * P];   // x rows
-    __shared__ __align__(16) T xd[Q * P];   // dte * x rows
-    __shared__ __align__(16) T hb[P * N];   // h_{c-1} rows p, pieces swizzled for 16-byte reads
-    // cs, ct, dte rows of a chunk; two objects so that reading one chunk's
-    // while the next one's copies are in flight needs no wait for them.
-    // (and the block factors, in the fourth 1 KB row).
-    __shared__ __align__(16) float tb0[4 * 256], tb1[4 * 256];
+    __shared__ __align__(16) char bl[Q * SB];  // B rows (token-major)
+    __shared__ __align__(16) char xs[Q * SX];  // x rows (token-major)
+    __shared__ __align__(16) char hb[P * SH];  // h_{c-1} in bf16, rows p
+    // Tables of a block; two objects, so that one block's are read while
+    // wave 0 writes the next block's.
+    __shared__ __align__(16) float tb0[kTbSize], tb1[kTbSize];
 
-    const int H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
+    const int H = p.nheads, G = p.ngroups, HPG = p.heads_per_group;
     const int PF = p.headdim, PS = PF / P;  // channels of a head, items per head
     const int64_t L = p.seqlen;
+    const int nb = (int)((L + Q - 1) / Q);
 
-    // ---- work of this workgroup (one per CU, persistent).  A unit is the
-    // chunks [cb, ce) of one item, (b, h, channel half s): item (b*H + h)*PS + s.  Workgroups are
-    // dealt to the XCDs in turn (w % 8), and each XCD takes a contiguous
-    // range of items, so that the heads sharing B and C rows run on one
-    // XCD and share its L2.  Within an XCD, with Ix items on Wx workgroups,
-    // each takes F = Ix / Wx whole items; the R = Ix % Wx left over are cut
-    // in two halves of their chunks when 2R <= Wx: workgroups 0..R-1 run a
-    // first half before their whole items, workgroups R..2R-1 a second half
-    // after theirs, taking the state entering it from the first half
-    // (written long before it is needed).  Every workgroup then runs F or
-    // F + 1/2 items' chunks instead of F or F + 1.
+    // ---- work of this workgroup.  A unit is an item (b, h, channel half s),
+    // item (b*H + h)*PS + s, with its blocks [c0, c1); blocks [0, c0) are
+    // run first for the state alone.  (Items fit 31 bits: the launcher
+    // checks.)
+    const int I = (int)(p.batch * H * PS);
     const int Wg = gridDim.x;
-    const int NX = Wg % kXcds == 0 ? kXcds : 1;
-    const int xcd = (int)blockIdx.x % NX, w = (int)blockIdx.x / NX, Wx = Wg / NX;
-    const int64_t I = p.batch * H * PS;
-    const int64_t Ibase = I / NX, Iext = I % NX;
-    const int64_t Ix = Ibase + (xcd < Iext ? 1 : 0);
-    const int64_t ibeg = xcd * Ibase + min((int64_t)xcd, Iext);  // first item of this XCD
-    const int F = (int)(Ix / Wx), R = (int)(Ix - (int64_t)F * Wx);
-    const bool split = F >= 1 && R > 0 && 2 * R <= Wx && nc >= 2;
-    const int nch = nc / 2;
-    const int nunits = F + (split ? (w < 2 * R ? 1 : 0) : (w < R ? 1 : 0));
+    const int NX = (Wg % kXcds == 0 && I >= kXcds) ? kXcds : 1;
+    const int xcd = (int)blockIdx.x % NX, wl = (int)blockIdx.x / NX, Wx = Wg / NX;
+    const int Ibase = I / NX, Iext = I % NX;
+    const int Ix = Ibase + (xcd < Iext ? 1 : 0);
+    const int ibeg = xcd * Ibase + min(xcd, Iext);  // first item of this XCD
     struct Unit {
-        int64_t item;
-        int cb, ce;
+        int item, c0, c1;
     };
+    int nunits = 0, F = 0, R = 0, S = 1;
+    bool split = false;
+    if (Ix >= Wx) {
+        F = Ix / Wx;
+        R = Ix - F * Wx;
+        split = R > 0 && 2 * R <= Wx && nb >= 2 && !p.no_split;
+        nunits = F + (split ? (wl < 2 * R ? 1 : 0) : (wl < R ? 1 : 0));
+    } else if (Ix > 0) {
+        S = p.no_split ? 1 : min(kMaxRanges, min(Wx / Ix, nb));
+        nunits = wl < Ix * S ? 1 : 0;
+    }
     auto unit = [&](int k) -> Unit {
-        if (split && w < R) {
-            if (k == 0) return Unit{ibeg + (int64_t)F * Wx + w, 0, nch};
-            return Unit{ibeg + w + (int64_t)Wx * (k - 1), 0, nc};
+        if (Ix < Wx) {
+            const int r = wl / Ix;
+            return Unit{ibeg + (wl - r * Ix), r * nb / S, (r + 1) * nb / S};
         }
-        if (split && w < 2 * R && k == F) return Unit{ibeg + (int64_t)F * Wx + (w - R), nch, nc};
-        return Unit{ibeg + w + (int64_t)Wx * k, 0, nc};
+        if (k < F) return Unit{ibeg + wl + Wx * k, 0, nb};
+        if (!split) return Unit{ibeg + F * Wx + wl, 0, nb};
+        if (wl < R) return Unit{ibeg + F * Wx + wl, 0, nb / 2};
+        return Unit{ibeg + F * Wx + (wl - R), nb / 2, nb};
     };
     if (nunits == 0) return;
-    // A step is one chunk of one unit; steps run in order k, then c.
-    // (b, h, g of the item are worked out once per unit; items fit 32 bits
-    // since batch and nheads are at most 65535.)
+    // A step is one block of one unit; units run in order, each from block 0.
+    // (b, h, g of the item are worked out once per unit.)
     struct Step {
-        int k, c;
-        int64_t item;
-        int cb, ce;
-        int64_t b, bh;  // bh = b*H + h
+        int k, c, c0, c1;
+        int item, b, bh;  // bh = b*H + h
         int h, g, s;
     };
-    auto step_of = [&](int k, int c) -> Step {
+    auto step_of = [&](int k) -> Step {
         const Unit u = unit(k);
         const uint32_t it = (uint32_t)u.item, bh = it / (uint32_t)PS, hh = bh % (uint32_t)H;
-        return Step{k,           c,        u.item,  u.cb, u.ce, (int64_t)(bh / (uint32_t)H), (int64_t)bh,
-                    (int)hh,     (int)hh / HPG, (int)(it - bh * (uint32_t)PS)};
+        return Step{k, 0, u.c0, u.c1, u.item, (int)(bh / (uint32_t)H), (int)bh, (int)hh, (int)hh / HPG,
+                    (int)(it - bh * (uint32_t)PS)};
     };
     auto next_step = [&](const Step &st) -> Step {
-        if (st.c + 1 < st.ce) {
+        if (st.c + 1 < st.c1) {
             Step n = st;
             n.c = st.c + 1;
             return n;
         }
-        return step_of(st.k + 1, unit(st.k + 1).cb);
+        return step_of(st.k + 1);
     };
     int nsteps = 0;
-    for (int k = 0; k < nunits; ++k) nsteps += unit(k).ce - unit(k).cb;
-
+    for (int k = 0; k < nunits; ++k) nsteps += unit(k).c1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int il = lane & 15, grp = lane >> 4;
-    const int tile = wide_tile<NIT>(wave), md = tile >> 1;
-    // Waves meet md off-diagonal blocks each, so the chunk lasts as long as
-    // the waves with the most; issue priority grows with md (0 .. 3), so the
-    // others fill the gaps (a SIMD's four waves together meet the same number).
-    const int prio = md * 4 / NBLK;
-    if (prio >= 3)
+    const int tile = wide_tile<kWaves>(wave), md = tile >> 1;
+    // Waves meet md off-diagonal blocks each, so a block lasts as long as the
+    // waves with the most; issue priority grows with md so that the others
+    // fill the gaps.
+    if (md >= 3)
         __builtin_amdgcn_s_setprio(3);
-    else if (prio == 2)
+    else if (md == 2)
         __builtin_amdgcn_s_setprio(2);
-    else if (prio == 1)
+    else if (md == 1)
         __builtin_amdgcn_s_setprio(1);
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
     const uint32_t HP2 = (uint32_t)H * PF * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
-    auto chunk_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
-    // Token rows of a step's chunk: x and y of its head, B and C of its group.
-    auto x_rows = [&](const Step &st) {
-        return rsrc((const T *)p.x + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
-                    chunk_len(st.c) * HP2);
+    auto block_len = [&](int c) -> int { return (int)min((int64_t)Q, L - (int64_t)c * Q); };
+    // Token rows of a step's block: x and y of its item, B and C of its
+    // group, dt of its head.  With on = false the descriptor covers no bytes:
+    // its loads read 0 and its stores are dropped, so that every step issues
+    // the same sequence of memory instructions (and the compiler's waits
+    // for loads in flight count exactly, without waiting for more).
+    auto x_rows = [&](const Step &st, bool on) {
+        return rsrc((const T *)p.x + (((int64_t)st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
+                    on ? block_len(st.c) * HP2 : 0u);
     };
-    auto y_rows = [&](const Step &st) {
-        return rsrc((const T *)p.y + ((st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
-                    chunk_len(st.c) * HP2);
+    auto y_rows = [&](const Step &st, bool on) {
+        return rsrc((const T *)p.y + (((int64_t)st.b * L + (int64_t)st.c * Q) * H + st.h) * PF + st.s * P,
+                    on ? block_len(st.c) * HP2 : 0u);
     };
-    auto b_rows = [&](const Step &st) {
-        return rsrc((const T *)p.B + ((st.b * L + (int64_t)st.c * Q) * G + st.g) * N, chunk_len(st.c) * GN2);
+    auto b_rows = [&](const Step &st, bool on) {
+        return rsrc((const T *)p.B + (((int64_t)st.b * L + (int64_t)st.c * Q) * G + st.g) * N,
+                    on ? block_len(st.c) * GN2 : 0u);
     };
-    auto c_rows = [&](const Step &st) {
-        return rsrc((const T *)p.C + ((st.b * L + (int64_t)st.c * Q) * G + st.g) * N, chunk_len(st.c) * GN2);
+    auto c_rows = [&](const Step &st, bool on) {
+        return rsrc((const T *)p.C + (((int64_t)st.b * L + (int64_t)st.c * Q) * G + st.g) * N,
+                    on ? block_len(st.c) * GN2 : 0u);
+    };
+    auto dt_rows = [&](const Step &st, bool on) {
+        return rsrc(p.dt + ((int64_t)st.b * L + (int64_t)st.c * Q) * H + st.h,
+                    on ? block_len(st.c) * (uint32_t)H * 4 : 0u);
     };
 
-    // ---- per-lane offsets, fixed for the whole loop.
-    // Global (bytes): the thread's 16-byte pieces of x and B rows, its C
-    // fragments (row 16 tile + il, columns 8grp + 32ks) and its y values
-    // (row 16 tile + il, columns 4grp + 16q).
-    const uint32_t vx = (uint32_t)(tid / WX) * HP2 + (tid % WX) * 16;
-    const uint32_t vb = (uint32_t)(tid / WB) * GN2 + (tid % WB) * 16;
-    const uint32_t vc = (uint32_t)(16 * tile + il) * GN2 + grp * 16;
-    const uint32_t vy = (uint32_t)(16 * tile + il) * HP2 + grp * 8;
-    // LDS (elements): where those x and B pieces go (piece swizzles depend on
-    // the row modulo 8, the same for all of a thread's pieces).
-    const int lx = (tid / WX) * P + 8 * ((tid % WX) ^ swz_tr<WX>(tid / WX));
-    const int lb = (tid / WB) * N + 8 * ((tid % WB) ^ swz_tr<WB>(tid / WB));
+    // ---- per-thread offsets of the global loads and of the LDS writes,
+    // recomputed where used from an opaque thread index (kept across the
+    // loop they would need registers): the thread's 16-byte pieces of x and
+    // B rows and its C fragments (row 16 tile + il, columns 8grp + 32ks).
+    auto otid = [&]() __attribute__((always_inline)) {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
 
     V8 xr[UXR], br[UBR];
-    Frag<T> cf[KS];  // C rows of the wave's tile (phase A and blue)
-    auto load_x = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = x_rows(st);
+    Frag<T> cf[KS];   // C rows of the wave's tile (G and blue)
+    auto load_x = [&](const Step &st, bool on) __attribute__((always_inline)) {
+        const auto r = x_rows(st, on);
+        const int t = otid();
+        const uint32_t vx = (uint32_t)(t / WX) * HP2 + (t % WX) * 16;
 #pragma unroll
         for (int u = 0; u < UXR; ++u)
             xr[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vx, u * RX * HP2, 0));
     };
-    auto load_b = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = b_rows(st);
+    auto load_b = [&](const Step &st, bool on) __attribute__((always_inline)) {
+        const auto r = b_rows(st, on);
+        const int t = otid();
+        const uint32_t vb = (uint32_t)(t / WB) * GN2 + (t % WB) * 16;
 #pragma unroll
         for (int u = 0; u < UBR; ++u)
             br[u] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, vb, u * RB * GN2, 0));
     };
-    auto load_c = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = c_rows(st);
+    auto load_c = [&](const Step &st, bool on) __attribute__((always_inline)) {
+        const auto r = c_rows(st, on);
+        const int t = otid() & 63;
+        const uint32_t vc = (uint32_t)(16 * tile + (t & 15)) * GN2 + (t >> 4) * 16;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc + 64 * ks, 0, 0));
+            cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc, 64 * ks, 0));
     };
-    // Table rows of chunk c (one 1 KB copy per table, waves 0-2) and its
-    // block factors (64 bytes, wave 3; its other lanes repeat the last piece).
-    static_assert(Cf::W >= 4, "four waves copy the tables");
-    auto issue_tables = [&](const Step &st, float *dst) __attribute__((always_inline)) {
-        const int64_t row = (st.bh * nc + st.c) * (int64_t)Q;  // tables are [b,H,nc,Q]
+    // dt of a step's tokens 2 lane and 2 lane + 1 (0 past the sequence),
+    // which wave 0 turns into tables; loaded by every wave so that the value
+    // is not a branch result.  Issued first at a switch, so that waiting for
+    // these two loads never waits for the others.
+    float dtr0, dtr1;
+    auto load_dt = [&](const Step &st, bool on) __attribute__((always_inline)) {
+        const auto r = dt_rows(st, on);
+        int ln = lane;  // opaque: recomputed here
+        asm volatile("" : "+v"(ln));
+        const uint32_t o = (uint32_t)(2 * ln) * H * 4;
+        dtr0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+        dtr1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o + H * 4, 0, 0));
+    };
+    // Wave 0: the tables of a step from its dt values (dtr0, dtr1).
+    // Prefix sums in fp64 (a wave-wide scan on the DPP row shifts and
+    // broadcasts), each table entry rounded once.
+    auto make_tables = [&](const Step &st, float *tb) __attribute__((always_inline)) {
+        const int Qc = block_len(st.c);
+        const double a = (double)((const __attribute__((address_space(4))) float *)(uintptr_t)p.A)[st.h];
+        // Opaque lane index: everything derived from it is computed here
+        // and not kept (or spilled) across the loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        if (wave < 3)
-            copy16_to_lds((wave == 0 ? p.cs : wave == 1 ? p.ct : p.dte) + row + 4 * min(ln, Q / 4 - 1),
-                          dst + 256 * wave);
-        else if (wave == 3)
-            copy16_to_lds(p.blk + (st.bh * nc + st.c) * (int64_t)kBlkStride + 4 * min(ln, kBlkStride / 4 - 1),
-                          dst + 768);
+        const int i0 = 2 * ln;
+        const float d0 = dtr0, d1 = dtr1;
+        double s0 = (double)d0, s1 = s0 + (double)d1;
+        // inclusive scan of the lane totals s1
+        double tot = s1;
+        auto dpp_add = [&](auto ctrl, auto rmask) __attribute__((always_inline)) {
+            constexpr int C = decltype(ctrl)::value, M = decltype(rmask)::value;
+            const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(tot), C, M, 0xf, true);
+            const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(tot), C, M, 0xf, true);
+            tot += __hiloint2double(hi, lo);
+        };
+        dpp_add(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});  // row_shr:1
+        dpp_add(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});  // row_shr:2
+        dpp_add(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});  // row_shr:4
+        dpp_add(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});  // row_shr:8
+        dpp_add(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});  // row_bcast:15
+        dpp_add(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});  // row_bcast:31
+        const double before = tot - s1;
+        s0 += before;
+        s1 += before;
+        // Sums at the ends of the 32-token blocks, e(m) = min(32m + 31, Qc - 1)
+        // (uniform lanes, read from their registers).
+        double se[kNBlk];
+#pragma unroll
+        for (int m = 0; m < kNBlk; ++m) {
+            const int e = min(kStep * m + kStep - 1, Qc - 1);
+            const double v = (e & 1) ? s1 : s0;
+            se[m] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), e >> 1),
+                                     __builtin_amdgcn_readlane(__double2loint(v), e >> 1));
+        }
+        const int mb = ln >> 4;  // the lane's 32-token block
+        const double sl = mb == 0 ? se[0] : mb == 1 ? se[1] : mb == 2 ? se[2] : se[3];
+        const bool in0 = i0 < Qc, in1 = i0 + 1 < Qc;
+        const float c0 = (float)(a * s0 * kLog2eD), c1 = (float)(a * s1 * kLog2eD);
+        *reinterpret_cast<float2 *>(tb + kTbCs2 + i0) = float2{c0, c1};
+        *reinterpret_cast<float2 *>(tb + kTbCt + i0) =
+            float2{in0 ? c0 - log2f(d0) : __builtin_inff(), in1 ? c1 - log2f(d1) : __builtin_inff()};
+        *reinterpret_cast<float2 *>(tb + kTbDte + i0) =
+            float2{in0 ? d0 * exp_neg((float)(a * (sl - s0))) : 0.f, in1 ? d1 * exp_neg((float)(a * (sl - s1))) : 0.f};
+        // Per 32-token block m (lane m < 4): cs2 at e(m) and the Horner factor
+        // exp(cs_e(m) - cs_e(m-1)) (exp(cs_e(0)) for m = 0).
+        if (ln < kNBlk) {
+            const int m = ln;
+            const double sm = m == 0 ? se[0] : m == 1 ? se[1] : m == 2 ? se[2] : se[3];
+            const double sp = m == 0 ? 0.0 : m == 1 ? se[0] : m == 2 ? se[1] : se[2];
+            tb[kTbCe + m] = (float)(a * sm * kLog2eD);
+            tb[kTbG + m] = exp_neg((float)(a * (sm - sp)));
+        }
     };
 
-    // ---- per-lane LDS offsets of the fragment reads (elements).  Every
-    // swizzle period divides 16 (rows) or 8 (tokens), so a fragment address
-    // is a per-lane constant plus a uniform base.
+    // ---- per-lane LDS bases of the fragment reads (bytes); every read adds
+    // an immediate offset.
     // Transposing reads (k = tokens): source lane il = 4kr + a points at
-    // token row 4grp + kr (and +16), columns 16t + 4a .. +3.
+    // token row 4grp + kr (and +16), columns 16t + 4a .. +3; lane il then
+    // holds column 16t + il of token rows 4grp + r (slots 0-3) and
+    // 16 + 4grp + r (slots 4-7).
     const int rl = 4 * grp + (il >> 2);
-    int xo[PT];  // x / xd fragments of p tile q
-#pragma unroll
-    for (int q = 0; q < PT; ++q) xo[q] = rl * P + 8 * ((2 * q + ((il & 3) >> 1)) ^ swz_tr<WX>(rl)) + 4 * (il & 1);
-    int xos[PTW];  // xd fragments of the wave's state p tiles
-#pragma unroll
-    for (int q = 0; q < PTW; ++q) {
-        const int t = pw * PTW + q;
-        xos[q] = rl * P + 8 * ((2 * t + ((il & 3) >> 1)) ^ swz_tr<WX>(rl)) + 4 * (il & 1);
-    }
-    int bo[NTW];  // B^T fragments of the wave's state n tiles
-#pragma unroll
-    for (int a = 0; a < NTW; ++a) {
-        const int t = nw * NTW + a;
-        bo[a] = rl * N + 8 * ((2 * t + ((il & 3) >> 1)) ^ swz_tr<WB>(rl)) + 4 * (il & 1);
-    }
-    // 16-byte row reads of B (phase A: rows 16a + il, piece 4ks + grp) and of
-    // h (blue: rows p = 16q + il, piece 4ks + grp).
-    int ro_b[KS], ro_h[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        ro_b[ks] = il * N + 8 * ((4 * ks + grp) ^ swz_tr<WB>(il));
-        ro_h[ks] = il * N + 8 * ((4 * ks + grp) ^ swz_rows16<WB>(il));
-    }
-    auto read_tr = [&](const T *base, int off, int ld) __attribute__((always_inline)) {
-        const i16x4 a0 = ds_read_tr16(base + off);
-        const i16x4 a1 = ds_read_tr16(base + 16 * ld + off);
+    const int xT = rl * SX + 8 * (il & 3);                      // x fragments (+32 per p tile)
+    const int bT = rl * SB + 8 * (il & 3) + 32 * nw * NTW;      // B^T fragments of the wave's state n tiles
+    const int xS = xT + 32 * pw * PTW;                          // x fragments of the wave's state p tiles
+    // 16-byte row reads: B (G: rows 16half + il, piece 4ks + grp) and h
+    // (blue: rows p = 16q + il, piece 4ks + grp).
+    const int bR = il * SB + 16 * grp;
+    const int hR = il * SH + 16 * grp;
+    auto lds16 = [&](const char *ptr) __attribute__((always_inline)) {
+        Frag<T> f;
+        f.v = *reinterpret_cast<const bf16x8 *>(ptr);
+        return f;
+    };
+    // Transposing read of two 16-token halves, `half` bytes apart.
+    auto read_tr = [&](const char *ptr, int half) __attribute__((always_inline)) {
+        const i16x4 a0 = ds_read_tr16(reinterpret_cast<const T *>(ptr));
+        const i16x4 a1 = ds_read_tr16(reinterpret_cast<const T *>(ptr + half));
         Frag<T> f;
         f.v = __builtin_bit_cast(bf16x8, i16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
         return f;
+    };
+    // The per-token factors of the lane's k slots in 32-token block m:
+    // tokens 32m + 4grp + r and 32m + 16 + 4grp + r.
+    auto slot_pair = [&](const float *row, int m, f32x4 &w0, f32x4 &w1) __attribute__((always_inline)) {
+        int g4 = 4 * grp;  // opaque: recomputed here rather than kept (or spilled) across the loop
+        asm volatile("" : "+v"(g4));
+        w0 = *reinterpret_cast<const f32x4 *>(row + kStep * m + g4);
+        w1 = *reinterpret_cast<const f32x4 *>(row + kStep * m + 16 + g4);
     };
 
     // ---- running state, tiles of S^T: hs[a][q][r] = h[p = 16(pw PTW + q) + il][n = 16(nw NTW + a) + 4grp + r]
@@ -318,148 +427,97 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
             for (int q = 0; q < PTW; ++q)
                 so[a][q] = (uint32_t)((16 * (pw * PTW + q) + (ln & 15)) * N + 16 * (nw * NTW + a) + 4 * (ln >> 4));
     };
-    // The item's state handed from a first half to a second half: its rows
-    // of entry [b, 0, h] of the workspace's chunk-state region, and its flag.
-    auto handoff_rsrc = [&](const Step &st) {
-        return buffer_rsrc(p.states + (((st.b * nc) * H + st.h) * PF + st.s * P) * (int64_t)N, (uint32_t)(P * N * 4));
+    // Accepted index of the item's sequence, clamped to [-1, L-1] (-1 when
+    // no state is asked for at an index).
+    auto j_of = [&](const Step &st) -> int64_t {
+        if (!p.state_out) return -2;
+        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[st.b];
+        return j < 0 ? -1 : min((int64_t)j, L - 1);
     };
-    int *handoff_flag = p.sync + kSyncHeader;
-    auto flag_of = [&](const Step &st) { return st.bh * kFlagsPerHead + st.s; };
-    bool gave_up = false;  // a hand-off wait timed out (the wave waits no more)
-    // Start a unit: h_{cb-1} is the initial state (or 0) for cb = 0, else
-    // the state the first half handed over.
+    // Start a unit: h_{-1} is the initial state (or 0).  The unit holding
+    // block 0 in its range also answers an accepted index of -1 (nothing
+    // accepted: the initial state).
     auto begin_unit = [&](const Step &st) __attribute__((always_inline)) {
         uint32_t so[NTW][PTW];
         state_offsets(so);
         // item * P * N = (bh * PF + s * P) * N: the item's rows of its head's state
-        const int64_t hst = st.item * (int64_t)P * N;
-        if (st.cb == 0) {
+        const int64_t hst = (int64_t)st.item * P * N;
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q)
+                hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (st.c0 == 0 && j_of(st) == -1) {
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
-                for (int q = 0; q < PTW; ++q)
-                    hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
-                                            : f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-            if (!gave_up && !wait_flag_device(handoff_flag + flag_of(st), kSpinLimit)) {
-                gave_up = true;
-                set_flag_device(p.sync + 1, 1);
-            }
-            const auto r = handoff_rsrc(st);
-#pragma unroll
-            for (int a = 0; a < NTW; ++a)
-#pragma unroll
-                for (int q = 0; q < PTW; ++q) hs[a][q] = load_f4_device(r, 4 * so[a][q]);
+                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.state_out + hst + so[a][q]) = hs[a][q];
         }
     };
-    // End a unit (hs = h_{ce-1}): the final state, or the hand-off.
+    // End a unit (hs = h_{c1-1}): the final state when the unit ends the item.
     auto end_unit = [&](const Step &st) __attribute__((always_inline)) {
-        uint32_t so[NTW][PTW];
-        state_offsets(so);
-        if (st.ce == nc) {
-            if (p.final_state) {
-                const int64_t hst = st.item * (int64_t)P * N;
-#pragma unroll
-                for (int a = 0; a < NTW; ++a)
-#pragma unroll
-                    for (int q = 0; q < PTW; ++q)
-                        *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
-            }
-        } else {
-            const auto r = handoff_rsrc(st);
+        if (st.c1 == nb && p.final_state) {
+            uint32_t so[NTW][PTW];
+            state_offsets(so);
+            const int64_t hst = (int64_t)st.item * P * N;
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
-                for (int q = 0; q < PTW; ++q) store_f4_device(r, 4 * so[a][q], hs[a][q]);
-            wait_vmcnt<0>();  // every store of this wave is visible device-wide ...
-            barrier_only();   // ... and of every wave
-            if (wave == 0) set_flag_device(handoff_flag + flag_of(st), 1);
+                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
         }
-    };
-    // Chunk whose entering state goes to hj (state_out at an index of -1 asks
-    // for the initial state, which enters chunk 0), and the skip weight.
-    auto cj_of = [&](const Step &st) {
-        if (!(p.hj && p.state_out_idx)) return -1;
-        const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[st.b];
-        return j < 0 ? 0 : (int)(min((int64_t)j, L - 1) / Q);
     };
     auto dh_of = [&](const Step &st) {
         return p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[st.h] : 0.f;
     };
 
-    // ---- per-chunk block factors (uniform).
-    float ce[NBLK];   // cs2 at the end of each block
-    float gst[NBLK];  // state Horner factors: exp(cs_e(0)), exp(cs_e(m) - cs_e(m-1))
+    // ---- per-block factors (uniform).
+    float ce[kNBlk];   // cs2 at the end of each 32-token block
+    float gst[kNBlk];  // state Horner factors
     int Qc = 0, nblk = 0;
-    bool live = false, has_prev = false;
+    bool live = false, full = false;
 
-    // Switch to chunk c: its x, B and tables have landed (and every wave has
-    // finished chunk c-1's LDS reads).
+    // Switch to a step: its x and B rows have landed, its tables are in tb
+    // (and every wave has finished the previous step's LDS reads).
     auto enter = [&](const Step &st, const float *tb) __attribute__((always_inline)) {
-        const int c = st.c;
-        Qc = chunk_len(c);
+        Qc = block_len(st.c);
         nblk = (Qc + kStep - 1) / kStep;
-        live = 16 * tile < Qc;
-        has_prev = c > 0 || p.init_state != nullptr;
-        // LDS: B rows, x and dte x rows (0 past the sequence), h_{c-1}.
+        full = st.c >= st.c0;
+        live = full && 16 * tile < Qc;
+        const int t = otid();
+        const int lx = (t / WX) * SX + 16 * (t % WX), lb = (t / WB) * SB + 16 * (t % WB);
 #pragma unroll
-        for (int u = 0; u < UBR; ++u) *reinterpret_cast<V8 *>(bl + lb + u * RB * N) = br[u];
+        for (int u = 0; u < UBR; ++u) *reinterpret_cast<V8 *>(bl + lb + u * RB * SB) = br[u];
 #pragma unroll
-        for (int u = 0; u < UXR; ++u) {
-            *reinterpret_cast<V8 *>(xs + lx + u * RX * P) = xr[u];
-            int t = tid;  // opaque copy: the row index is recomputed here, not kept (or spilled)
-            asm volatile("" : "+v"(t));
-            const float d = tb[512 + t / WX + u * RX];
-            V8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (T)(d * (float)xr[u][e]);
-            *reinterpret_cast<V8 *>(xd + lx + u * RX * P) = v;
-        }
-        if (has_prev) {
+        for (int u = 0; u < UXR; ++u) *reinterpret_cast<V8 *>(xs + lx + u * RX * SX) = xr[u];
+        if (full && (st.c > 0 || p.init_state)) {  // blue reads h_{c-1} in bf16
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
                 for (int q = 0; q < PTW; ++q) {
                     const int pp = 16 * (pw * PTW + q) + il, n = 16 * (nw * NTW + a) + 4 * grp;
-                    *reinterpret_cast<V4 *>(hb + pp * N + 8 * ((n >> 3) ^ swz_rows16<WB>(pp)) + (n & 7)) =
+                    *reinterpret_cast<V4 *>(hb + pp * SH + 2 * n) =
                         V4{(T)hs[a][q][0], (T)hs[a][q][1], (T)hs[a][q][2], (T)hs[a][q][3]};
                 }
         }
-        if (c == cj_of(st)) {
-            uint32_t so[NTW][PTW];
-            state_offsets(so);
-            const int64_t hst = st.item * (int64_t)P * N;
 #pragma unroll
-            for (int a = 0; a < NTW; ++a)
-#pragma unroll
-                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.hj + hst + so[a][q]) = hs[a][q];
-        }
-        // Block factors of the chunk (copied with the tables; uniform).
-#pragma unroll
-        for (int m = 0; m < NBLK; ++m) {
-            ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[768 + m])));
-            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[768 + kBlkStride / 2 + m])));
+        for (int m = 0; m < kNBlk; ++m) {
+            ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[kTbCe + m])));
+            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[kTbG + m])));
         }
     };
 
-    // One chunk (tables in tb): blue, orange and D skip, stored; then the state.
-    auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb) __attribute__((always_inline)) {
-        const int c = st.c;
+    // Blue, orange and the D skip of a full step, for the wave's rows.
+    auto outputs = [&](const Step &st, const float *tb, f32x4 (&acc)[PT]) __attribute__((always_inline)) {
         const float dh = dh_of(st);
-        const float cs2i = tb[16 * tile + il] * kLog2e;
-        f32x4 acc[PT];
-#pragma unroll
-        for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bool has_prev = st.c > 0 || p.init_state != nullptr;
+        const float cs2i = tb[kTbCs2 + 16 * tile + il];
         // Blue: exp(cs_i) C_i . h_{c-1} (rows p, column i).
-        if (has_prev && live) {
+        if (has_prev) {
 #pragma unroll
             for (int q = 0; q < PT; ++q)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    Frag<T> hf;
-                    load8(hf, hb + 16 * q * N + ro_h[ks]);
-                    mma(hf, cf[ks], acc[q]);
-                }
+                for (int ks = 0; ks < KS; ++ks) mma(lds16(hb + hR + 16 * q * SH + 64 * ks), cf[ks], acc[q]);
             const float ei = exp2_hw(cs2i);
 #pragma unroll
             for (int q = 0; q < PT; ++q) acc[q] = acc[q] * ei;
@@ -469,55 +527,51 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
         auto g_half = [&](int m, int half) __attribute__((always_inline)) {
             f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                Frag<T> bf;
-                load8(bf, bl + (kStep * m + 16 * half) * N + ro_b[ks]);
-                mma(bf, cf[ks], a4);
-            }
+            for (int ks = 0; ks < KS; ++ks) mma(lds16(bl + bR + (kStep * m + 16 * half) * SB + 64 * ks), cf[ks], a4);
             return a4;
         };
-        // Orange off the diagonal: G times its row factor
-        // exp2(cs2_i - cs2_e(m)) <= 1, rounded to bf16 once, on dte x.
-        static_for<NBLK - 1>([&](auto mc) __attribute__((always_inline)) {
+        // Orange below the diagonal block: G times exp2(cs2_i - cs2_e(m)) dte_j,
+        // rounded to bf16 once, on raw x.
+        static_for<kNBlk - 1>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
-            if (!live || m >= md) return;
+            if (m >= md) return;
             const float ai = exp2_hw(cs2i - ce[m]);
+            f32x4 w0, w1;
+            slot_pair(tb + kTbDte, m, w0, w1);
             Frag<T> gf;
+            const f32x4 g0 = g_half(m, 0);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x4 a4 = g_half(m, half);
+            for (int r = 0; r < 4; ++r) gf.set(r, g0[r] * (ai * w0[r]));
+            const f32x4 g1 = g_half(m, 1);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gf.set(4 * half + r, a4[r] * ai);
-            }
+            for (int r = 0; r < 4; ++r) gf.set(4 + r, g1[r] * (ai * w1[r]));
 #pragma unroll
-            for (int q = 0; q < PT; ++q) mma(read_tr(xd + kStep * m * P, xo[q], P), gf, acc[q]);
+            for (int q = 0; q < PT; ++q) mma(read_tr(xs + xT + kStep * m * SX + 32 * q, 16 * SX), gf, acc[q]);
         });
         // Diagonal block md: G times the exact factors exp2(cs2_i - ct_j)
         // (the exponent is at most log2(dt_j) for j <= i; above the diagonal
-        // it is set to -inf, which masks G), plus D at j = i (the skip term),
+        // the product is replaced by 0), plus D at j = i (the skip term),
         // rounded to bf16 once, on raw x.  j - i = 16 half + r - di, with di
         // from an opaque copy so that the comparisons are made here and not
-        // kept across the chunk loop.
-        if (live) {
+        // kept across the loop.
+        {
             int di = 16 * (tile & 1) + il - 4 * grp;
             asm volatile("" : "+v"(di));
-            int g4 = 4 * grp;  // opaque: recomputed here rather than kept (or spilled) across the loop
-            asm volatile("" : "+v"(g4));
-            const f32x4 ct0 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + g4);
-            const f32x4 ct1 = *reinterpret_cast<const f32x4 *>(tb + 256 + kStep * md + 16 + g4);
-            const float ninf = -__builtin_inff();
+            f32x4 ct0, ct1;
+            slot_pair(tb + kTbCt, md, ct0, ct1);
             Frag<T> lf;
             const f32x4 g0 = g_half(md, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float v = g0[r] * exp2_hw(r > di ? ninf : cs2i - ct0[r]);
+                // above the diagonal the factor may overflow; the select drops it
+                const float v = r > di ? 0.f : g0[r] * exp2_hw(cs2i - ct0[r]);
                 lf.set(r, r == di ? v + dh : v);
             }
             if (tile & 1) {
                 const f32x4 g1 = g_half(md, 1);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float v = g1[r] * exp2_hw(16 + r > di ? ninf : cs2i - ct1[r]);
+                    const float v = 16 + r > di ? 0.f : g1[r] * exp2_hw(cs2i - ct1[r]);
                     lf.set(4 + r, 16 + r == di ? v + dh : v);
                 }
             } else {
@@ -525,17 +579,19 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                 for (int r = 0; r < 4; ++r) lf.set(4 + r, 0.f);  // rows above the diagonal
             }
 #pragma unroll
-            for (int q = 0; q < PT; ++q) mma(read_tr(xs + kStep * md * P, xo[q], P), lf, acc[q]);
+            for (int q = 0; q < PT; ++q) mma(read_tr(xs + xT + kStep * md * SX + 32 * q, 16 * SX), lf, acc[q]);
         }
-        // y, rounded; rows past the sequence fall outside the buffer.  y is
-        // written once and not read here: non-temporal stores (kAuxNt) keep
-        // it from displacing the B and C rows the other heads still read.
-        // Lane (il, grp) holds channels 16q + 4grp .. +3 of row il; the four
-        // lanes of a row swap values so that lane g holds channels
-        // 32k + 8g .. +7 for k < PT/2 and each store writes 64 contiguous
-        // bytes of every row (whole 64-byte pieces, no partial writes).
-        if (live) {
-            const auto r = y_rows(st);
+    };
+    // y, rounded; rows past the sequence fall outside the buffer (and with
+    // on = false every store is dropped).  y is written once and not read
+    // here: non-temporal stores keep it from displacing the B and C rows the
+    // other heads still read.  Lane (il, grp) holds channels 16q + 4grp .. +3
+    // of row il; the four lanes of a row swap values so that lane g holds
+    // channels 32k + 8g .. +7 for k < PT/2 and each store writes 64
+    // contiguous bytes of every row.
+    auto store_y = [&](const Step &st, bool on, const f32x4 (&acc)[PT]) __attribute__((always_inline)) {
+        {
+            const auto r = y_rows(st, on);
             int ln = lane;  // opaque: the shuffle sources are recomputed here
             asm volatile("" : "+v"(ln));
             const int g = ln >> 4, s0 = ((ln & 15) + 32 * (g & 1)) << 2, s1 = s0 + 64;
@@ -558,17 +614,75 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                 __builtin_amdgcn_raw_buffer_store_b128((g >> 1) ? w[1] : w[0], r, vyr + 64 * k, 0, kAuxNt);
             }
         }
-        // C rows of the next chunk (cf is no longer needed).
-        if (has_next) load_c(nx);
-        // State: h_c = exp(cs_last) h_{c-1} + B^T (w x), Horner over the blocks.
-        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
+    };
+
+    // One step (tables in tb): the state (and the state after the accepted
+    // index if it lies in the step), then the outputs if the step is full.
+    // The state part comes first so that its products cover the latency of
+    // the C rows, fetched at the switch into the step; the y stores come
+    // last, and nothing waits for them.
+    auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
+        __attribute__((always_inline)) {
+        // Wave 0: the next step's tables first (its dt values were fetched at
+        // the switch into this step), at top issue priority, so that they
+        // are never waited for.
+        if (has_next && wave == 0) {
+            __builtin_amdgcn_s_setprio(3);
+            make_tables(nx, tb_next);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        // Accepted index j in this step: its 32-token block mj and its
+        // position jl in the step (uniform; -1 if not here).
+        int jl = -1;
+        if (full) {
+            const int64_t j = j_of(st);
+            if (j >= 0 && j / Q == st.c) jl = (int)(j - (int64_t)st.c * Q);
+        }
+        const int mj = jl >= 0 ? jl / kStep : -1;
+        // State: h_c = exp(cs_last) h_{c-1} + B^T (w x), Horner over the
+        // 32-token blocks.  In the block mj holding j, first the state after
+        // j: the state at the end of the previous 32-token block times
+        // exp(cs_j - cs_e(mj-1)) plus the tokens s <= j of block mj with
+        // their exact factors exp2(cs2_j - ct_s), stored to state_out.
+        static_for<kNBlk>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
             if (m >= nblk) return;
             Frag<T> fa[NTW], fb[PTW];
 #pragma unroll
-            for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + kStep * m * N, bo[a], N);
+            for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + bT + kStep * m * SB + 32 * a, 16 * SB);
 #pragma unroll
-            for (int q = 0; q < PTW; ++q) fb[q] = read_tr(xd + kStep * m * P, xos[q], P);
+            for (int q = 0; q < PTW; ++q) fb[q] = read_tr(xs + xS + kStep * m * SX + 32 * q, 16 * SX);
+            if (m == mj) {
+                const float cs2j = tb[kTbCs2 + jl];
+                const float ej = exp2_hw(m == 0 ? cs2j : cs2j - ce[m > 0 ? m - 1 : 0]);
+                int j4 = jl - 4 * grp;  // slot r of half 0 is token 32m + 4grp + r
+                asm volatile("" : "+v"(j4));
+                f32x4 c0, c1, w0, w1;
+                slot_pair(tb + kTbCt, m, c0, c1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    w0[r] = kStep * m + r > j4 ? 0.f : exp2_hw(cs2j - c0[r]);
+                    w1[r] = kStep * m + 16 + r > j4 ? 0.f : exp2_hw(cs2j - c1[r]);
+                }
+                uint32_t so[NTW][PTW];
+                state_offsets(so);
+                float *dst = p.state_out + (int64_t)st.item * P * N;
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) {
+                    Frag<T> fw = fb[q];
+                    scale_frag(fw, w0, w1);
+#pragma unroll
+                    for (int a = 0; a < NTW; ++a) {
+                        f32x4 hv = hs[a][q] * ej;
+                        mma(fa[a], fw, hv);
+                        *reinterpret_cast<f32x4 *>(dst + so[a][q]) = hv;
+                    }
+                }
+            }
+            f32x4 w0, w1;
+            slot_pair(tb + kTbDte, m, w0, w1);
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) scale_frag(fb[q], w0, w1);
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -577,99 +691,101 @@ __global__ __launch_bounds__(64 * NIT) void chunk_scan_fused_kernel(Params p) {
                     mma(fa[a], fb[q], hs[a][q]);
                 }
         });
+        {
+            f32x4 acc[PT];
+#pragma unroll
+            for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (live) outputs(st, tb, acc);
+            store_y(st, live, acc);
+        }
     };
 
-    // ---- prologue: the first step's inputs.
-    Step cur = step_of(0, unit(0).cb);
-    issue_tables(cur, tb0);
-    load_x(cur);
-    load_b(cur);
-    load_c(cur);
+    // ---- prologue: the first step's inputs and tables.  The tables of
+    // step s are in tb0 / tb1 for s even / odd, made by wave 0 at the start
+    // of step s - 1 from the dt values fetched at the switch into it.
+    Step cur = step_of(0);
+    load_dt(cur, true);
+    load_x(cur, true);
+    load_b(cur, true);
     wait_vmcnt<0>();
-    barrier_only();  // every wave's table copies have landed
+    if (wave == 0) make_tables(cur, tb0);
+    lds_barrier();  // the tables are written
     begin_unit(cur);
     enter(cur, tb0);
-    if (nsteps > 1) {
-        const Step nx = next_step(cur);
-        load_x(nx);
-        load_b(nx);
-        issue_tables(nx, tb1);
+    {
+        // In this order: what the step needs soonest is fetched first, since
+        // a wave's vector memory operations complete in issue order.
+        const Step nx = nsteps > 1 ? next_step(cur) : cur;
+        load_dt(nx, nsteps > 1);
+        load_c(cur, cur.c >= cur.c0);
+        load_x(nx, nsteps > 1);
+        load_b(nx, nsteps > 1);
     }
     lds_barrier();
 
-    // ---- steps, two per iteration so that each table buffer is a
-    // compile-time choice.
-    for (int s0 = 0; s0 < nsteps; s0 += 2) {
-        static_for<2>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int K = decltype(kc)::value;
-            const int s = s0 + K;
-            if (s >= nsteps) return;
-            const bool has_next = s + 1 < nsteps;
-            const Step nx = has_next ? next_step(cur) : cur;
-            compute(cur, has_next, nx, K == 0 ? tb0 : tb1);
-            // The next step's loads and copies were issued before this
-            // step's C rows; wait for all of them (after the last step too,
-            // so that on every path into the next iteration the C rows have
-            // landed and the compiler adds no wait for them).
-            wait_vmcnt<0>();
-            if (cur.c + 1 == cur.ce) end_unit(cur);
-            if (has_next) {
-                lds_barrier();  // every wave has finished this step's LDS reads
-                if (nx.c == nx.cb) begin_unit(nx);
-                enter(nx, K == 0 ? tb1 : tb0);
-                if (s + 2 < nsteps) {
-                    const Step nn = next_step(nx);
-                    load_x(nn);
-                    load_b(nn);
-                    issue_tables(nn, K == 0 ? tb0 : tb1);
-                }
-                lds_barrier();
-                cur = nx;
-            }
-        });
-    }
-}
-
-template <int NT, int PT, int NIT>
-hipError_t launch_cfg(const Params &p, hipStream_t stream) {
-    using Cf = FusedCfg<NT, PT, NIT>;
-    if constexpr (!Cf::OK) {
-        return hipErrorNotSupported;
-    } else {
-        // One workgroup per CU (each takes one CU's LDS); never more than items.
-        const int64_t items = p.batch * p.nheads * (p.headdim / Cf::P);
-        const int64_t grid = std::min<int64_t>(items, compute_units());
-        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, NIT>), dim3((unsigned)grid), dim3(Cf::THREADS), 0,
-                           stream, p);
-        return hipGetLastError();
+    // ---- steps.
+    for (int s = 0; s < nsteps; ++s) {
+        const bool has_next = s + 1 < nsteps;
+        const Step nx = has_next ? next_step(cur) : cur;
+        float *tbc = (s & 1) ? tb1 : tb0, *tbn = (s & 1) ? tb0 : tb1;
+        compute(cur, has_next, nx, tbc, tbn);
+        // Wait for the next step's x and B rows, not for this step's y
+        // stores issued after them: a wave's vector memory operations
+        // complete in the order they were issued.
+        wait_vmcnt<PT / 2>();
+        if (cur.c + 1 == cur.c1) end_unit(cur);
+        if (has_next) {
+            lds_barrier();  // every wave has finished this step's LDS reads; next tables written
+            if (nx.c == 0) begin_unit(nx);
+            enter(nx, tbn);
+            const bool more = s + 2 < nsteps;
+            const Step nn = more ? next_step(nx) : nx;
+            load_dt(nn, more);
+            load_c(nx, nx.c >= nx.c0);
+            load_x(nn, more);
+            load_b(nn, more);
+            lds_barrier();
+            cur = nx;
+        }
     }
 }
 
 template <int NT, int PT>
-hipError_t dispatch_q(const Params &p, hipStream_t stream) {
-    switch (p.chunk) {
-        case 128: return launch_cfg<NT, PT, 8>(p, stream);
-        case 256: return launch_cfg<NT, PT, 16>(p, stream);
-        default: return hipErrorNotSupported;
+hipError_t launch_cfg(const Params &p, hipStream_t stream) {
+    using Cf = FusedCfg<NT, PT>;
+    if constexpr (!Cf::OK) {
+        return hipErrorNotSupported;
+    } else {
+        // Two workgroups per compute unit (each under half a CU's LDS).
+        const int grid = 2 * compute_units();
+        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
     }
 }
 
 template <int NT>
 hipError_t dispatch_p(const Params &p, hipStream_t stream) {
     switch (p.headdim) {
-        case 32: return dispatch_q<NT, 2>(p, stream);
-        case 64: return dispatch_q<NT, 4>(p, stream);
-        case 128: return dispatch_q<NT, 4>(p, stream);  // two 64-channel items per head
+        case 32: return launch_cfg<NT, 2>(p, stream);
+        case 64: return launch_cfg<NT, 4>(p, stream);
+        case 128: return launch_cfg<NT, 4>(p, stream);  // two 64-channel items per head
         default: return hipErrorNotSupported;
     }
 }
 
 }  // namespace
 
+bool chunk_scan_fused_takes(const Params &p) {
+    const int64_t items = p.batch * p.nheads * (p.headdim == 128 ? 2 : 1);
+    // 32-bit byte offsets of one block's rows of x and y.
+    const int64_t row_bytes = (int64_t)p.nheads * p.headdim * 2;
+    return items >= kFusedMinItems && items < ((int64_t)1 << 30) && p.seqlen >= 1 &&
+           row_bytes * kQ < ((int64_t)1 << 31) && (int64_t)p.ngroups * p.dstate * 2 * kQ < ((int64_t)1 << 31) &&
+           (p.dstate == 64 || p.dstate == 128) && (p.headdim == 32 || p.headdim == 64 || p.headdim == 128);
+}
+
 hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream) {
-    // One workgroup per item and one CU each: with fewer than a CU's worth
-    // of them the chunk-parallel kernels use the GPU better.
-    if (p.batch * p.nheads * (p.headdim == 128 ? 2 : 1) < kFusedMinHeads) return hipErrorNotSupported;
+    if (!chunk_scan_fused_takes(p)) return hipErrorNotSupported;
     switch (p.dstate) {
         case 64: return dispatch_p<4>(p, stream);
         case 128: return dispatch_p<8>(p, stream);

@@ -45,6 +45,7 @@ struct Params {
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
+    int no_split;             // single pass: run every item whole on one workgroup (in-place calls)
 };
 
 // Each launcher enqueues one kernel on `stream` and returns hipGetLastError().
@@ -59,13 +60,16 @@ hipError_t launch_chunk_output(const Params &p, Elem e, hipStream_t stream);
 // shape does not fit its LDS budget (the caller then uses launch_chunk_output).
 hipError_t launch_chunk_output_heads(const Params &p, hipStream_t stream);
 hipError_t launch_state_at_index(const Params &p, Elem e, hipStream_t stream);
-// Single-pass bf16 forward: a persistent grid in which one workgroup at a
-// time runs every chunk of an item ((b, h), or a 64-channel half of a head of
-// headdim 128) in order with the state in registers (after
-// launch_chunk_cumsum; writes y, final_state and, with state_out, hj).
-// Returns hipErrorNotSupported for shapes it does not take or with fewer
-// than kFusedMinHeads items.
-constexpr int64_t kFusedMinHeads = 256;
+// Single-pass bf16 forward: one kernel for the whole call (its own
+// chunk-local tables from dt and A; y, final_state and state_out written
+// directly; the workspace is not used).  A grid of two workgroups per
+// compute unit in which one workgroup at a time runs an item ((b, h), or a
+// 64-channel half of a head of headdim 128), or a range of its blocks, in
+// order with the state in registers.  chunk_scan_fused_takes says whether
+// it takes a call; launch_chunk_scan_fused returns hipErrorNotSupported for
+// calls it does not take.
+constexpr int64_t kFusedMinItems = 64;
+bool chunk_scan_fused_takes(const Params &p);
 hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream);
 // Whole forward of a one-chunk call of at most 32 tokens in one kernel (y,
 // final_state, state_out; the workspace is not used).  Returns

@@ -269,6 +269,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.chunk = chunk_size;
     p.nchunks = (int)L.nc;
     p.heads_per_group = (int)(H / G);
+    p.no_split = in_place ? 1 : 0;
     const ssd::Elem e = dtype == SSD_DTYPE_BF16 ? ssd::Elem::BF16 : ssd::Elem::F32;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
@@ -280,10 +281,10 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     } else if (run.try_step("one_chunk", [&] { return ssd::launch_one_chunk(p, e, stream); })) {
         // short call: the whole forward in one kernel
     } else {
+        if (e == ssd::Elem::BF16 && ssd::chunk_scan_fused_takes(p)) {
+            run.step("chunk_scan_fused", [&] { return ssd::launch_chunk_scan_fused(p, stream); });
+        } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
-        const bool fused = e == ssd::Elem::BF16 &&
-                           run.try_step("chunk_scan_fused", [&] { return ssd::launch_chunk_scan_fused(p, stream); });
-        if (!fused) {
         run.step("chunk_state", [&] {
             if (e == ssd::Elem::BF16) {
                 const hipError_t r = ssd::launch_chunk_state_heads(p, stream);
@@ -299,8 +300,8 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
             }
             return ssd::launch_chunk_output(p, e, stream);
         });
-        }
         if (state_out) run.step("state_at_index", [&] { return ssd::launch_state_at_index(p, e, stream); });
+        }
     }
     if (run.err != hipSuccess)
         return fail(SSD_ERR_HIP, "%s launch failed: %s", run.failed_step, hipGetErrorString(run.err));

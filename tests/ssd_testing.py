@@ -64,6 +64,8 @@ def gpu_run(inp, chunk=None, use_D=True, use_init=True, use_state_out=True, dev=
     ws = torch.empty(max(ssd.ssd_workspace_bytes(shape, chunk, code), 1), dtype=torch.uint8, device=dev["x"].device)
     if fill_workspace is not None:
         ws.fill_(fill_workspace)
+    elif return_workspace:
+        ws.zero_()  # regions the path that runs leaves unwritten read as zeros, not as leftover bits
     y, fin, sout = ssd.ssd_chunk_scan_fwd(
         dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"] if use_D else None,
         dev["init_state"] if use_init else None, chunk,
@@ -73,7 +75,6 @@ def gpu_run(inp, chunk=None, use_D=True, use_init=True, use_state_out=True, dev=
     if return_workspace:
         cs, st, prev = ssd.workspace_views(ws, shape, chunk, code)
         out["cs"], out["states"], out["prev"] = to_np(cs), to_np(st), to_np(prev)
-        out["timeout"] = timeout_word(ws, shape, chunk, code)
     return out
 
 
@@ -90,12 +91,6 @@ def kernel_names(inp, chunk=None, dev=None):
                                               marks=[e.cuda_event for e in evs])
     torch.cuda.synchronize()
     return names
-
-
-def timeout_word(ws, shape, chunk, code) -> int:
-    """The workspace word a wait for a handed-over state sets when it gives up."""
-    lay = ssd.ssd_get_workspace_layout(shape, chunk, code)
-    return int(ws[lay.sync_offset + 4:lay.sync_offset + 8].view(torch.int32).item())
 
 
 def oracle_run(inp, use_D=True, use_init=True, use_state_out=True, chunk=0):
