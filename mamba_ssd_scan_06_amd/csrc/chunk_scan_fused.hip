@@ -31,8 +31,8 @@
 //     once, on raw x; exact however strong the decay inside the block;
 //   blue: exp2(cs2_i) times C_i . h_{c-1};
 //   state, in Horner form over the 32-token blocks: acc = acc g_m +
-//     B_m^T (dte x)_m with g_0 = exp(cs_e(0)), g_m = exp(cs_e(m) - cs_e(m-1));
-//     dte x is formed from the transposed x fragment and rounded once.
+//     (dte B)_m^T x_m with g_0 = exp(cs_e(0)), g_m = exp(cs_e(m) - cs_e(m-1));
+//     dte B is formed from the transposed B fragment and rounded once.
 // The state after an accepted index j (multi-step verify, "3天把Llama训成
 // Mamba", blog.csdn.net, section "推测解码") is computed in the block holding
 // j, from the state entering it, with the exact factors exp2(cs2_j - ct_s):
@@ -73,18 +73,10 @@ namespace ssd {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kQ = 128;             // tokens per block
 constexpr int kStep = 32;           // tokens per j block (one MFMA k step)
-constexpr int kNBlk = kQ / kStep;   // 32-token blocks per block
-constexpr int kWaves = 8;           // one 16-row tile per wave
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxRanges = 4;       // ranges per item when items are fewer than workgroups
 constexpr int kAuxNt = 2;           // cache-policy operand of the buffer builtins: nt (non-temporal)
 constexpr double kLog2eD = 1.4426950408889634074;
-// Per-block tables in LDS (floats): cs2, ct, dte per token, then cs2 at the
-// end of each 32-token block and the Horner factors.
-constexpr int kTbCs2 = 0, kTbCt = kQ, kTbDte = 2 * kQ, kTbCe = 3 * kQ, kTbG = 3 * kQ + kNBlk;
-constexpr int kTbSize = 3 * kQ + 2 * kNBlk;
 
 // Compute units of the current device (cached per device).
 int compute_units() {
@@ -99,24 +91,38 @@ int compute_units() {
     return cached[dev];
 }
 
-template <int NT, int PT>
+// Geometry for dstate 16 NT, item channels 16 PT and blocks of QB tokens:
+// QB / 16 waves, one 16-row tile each.
+template <int NT, int PT, int QB>
 struct FusedCfg {
-    static constexpr int N = NT * 16, P = PT * 16, Q = kQ;
-    static constexpr int KS = N / 32;                 // 32-wide k steps over n
-    static constexpr int WB = N / 8, WX = P / 8;      // 16-byte pieces per B row, per x row
-    static constexpr int WPP = 2, WPN = kWaves / WPP; // waves along p, n (state tiles)
+    static constexpr int N = NT * 16, P = PT * 16, Q = QB;
+    static constexpr int W = Q / 16, THREADS = 64 * W;  // waves, threads
+    static constexpr int NBLK = Q / kStep;              // 32-token blocks per block
+    static constexpr int TPL = Q / 64;                  // tokens per lane in the table wave
+    static constexpr int KS = N / 32;                   // 32-wide k steps over n
+    static constexpr int WB = N / 8, WX = P / 8;        // 16-byte pieces per B row, per x row
+    // Waves along n and p over the 16x16 tiles of the state: all of n
+    // first, so that each B fragment of the state update, scaled by the
+    // per-token decay, is read (and scaled) by one wave only.
+    static constexpr int WPN = NT >= W ? W : NT, WPP = W / WPN;
     static constexpr int NTW = NT / WPN, PTW = PT / WPP;
-    static constexpr int UXR = Q * WX / kThreads;     // 16-byte x pieces per thread
-    static constexpr int UBR = Q * WB / kThreads;     // 16-byte B pieces per thread
+    static constexpr int UXR = Q * WX / THREADS;        // 16-byte x pieces per thread
+    static constexpr int UBR = Q * WB / THREADS;        // 16-byte B pieces per thread
+    // Per-block tables in LDS (floats): cs2, ct, dte per token, then cs2 at
+    // the end of each 32-token block and the Horner factors.
+    static constexpr int TB_CS2 = 0, TB_CT = Q, TB_DTE = 2 * Q, TB_CE = 3 * Q, TB_G = 3 * Q + NBLK;
+    static constexpr int TB_SIZE = 3 * Q + 2 * NBLK;
     // LDS rows are padded by 32 bytes: 16 lanes reading 16 bytes of 16
     // consecutive rows, and the transposing reads of 4 consecutive rows,
     // then spread over the banks, and every fragment address is one
     // per-lane base plus an immediate offset.
     static constexpr int SB = N * 2 + 32, SX = P * 2 + 32, SH = N * 2 + 32;  // bytes per LDS row of B, x, h
-    static constexpr size_t LDS_BYTES = (size_t)Q * SB + (size_t)Q * SX + (size_t)P * SH + 2 * kTbSize * 4;
-    static constexpr bool OK = NT % WPN == 0 && PT % WPP == 0 && NTW >= 1 && PTW >= 1 && UXR >= 1 && UBR >= 1 &&
-                               (Q * WX) % kThreads == 0 && (Q * WB) % kThreads == 0 && LDS_BYTES <= 80 * 1024;
-    static_assert(!OK || LDS_BYTES <= 81920, "two workgroups per compute unit");
+    static constexpr size_t LDS_BYTES = (size_t)Q * SB + (size_t)Q * SX + (size_t)P * SH + 2 * TB_SIZE * 4;
+    // Two workgroups per compute unit when two fit its 160 KB of LDS.
+    static constexpr int WGS_PER_CU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
+    static constexpr bool OK = NTW >= 1 && PTW >= 1 && NT % WPN == 0 && PT % WPP == 0 && UXR >= 1 && UBR >= 1 &&
+                               (Q * WX) % THREADS == 0 && (Q * WB) % THREADS == 0 && LDS_BYTES <= 160 * 1024 &&
+                               W * WGS_PER_CU == 16;
 };
 
 // Raw buffer descriptor over [base, base + bytes): loads beyond it read 0
@@ -142,15 +148,18 @@ __device__ __forceinline__ void scale_frag(Frag<bf16> &f, const f32x4 &w0, const
     }
 }
 
-template <int NT, int PT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+template <int NT, int PT, int QB>
+__global__ __launch_bounds__(4 * QB) __attribute__((amdgpu_waves_per_eu(4)))  // QB / 16 waves
 void chunk_scan_fused_kernel(Params p) {
-    using Cf = FusedCfg<NT, PT>;
+    using Cf = FusedCfg<NT, PT, QB>;
     using T = bf16;
-    constexpr int N = Cf::N, P = Cf::P, Q = kQ, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
+    constexpr int N = Cf::N, P = Cf::P, Q = Cf::Q, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
+    constexpr int W = Cf::W, THREADS = Cf::THREADS, NBLK = Cf::NBLK, TPL = Cf::TPL;
+    static_assert(THREADS == 4 * QB, "launch bounds");
+    constexpr int TB_CS2 = Cf::TB_CS2, TB_CT = Cf::TB_CT, TB_DTE = Cf::TB_DTE, TB_CE = Cf::TB_CE, TB_G = Cf::TB_G;
     constexpr int NTW = Cf::NTW, PTW = Cf::PTW, UXR = Cf::UXR, UBR = Cf::UBR;
     constexpr int SB = Cf::SB, SX = Cf::SX, SH = Cf::SH;
-    constexpr int RX = kThreads / WX, RB = kThreads / WB;  // rows between a thread's x / B pieces
+    constexpr int RX = THREADS / WX, RB = THREADS / WB;  // rows between a thread's x / B pieces
     typedef typename Vec8<T>::type V8;
     typedef typename Vec4<T>::type V4;
     typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -160,7 +169,7 @@ void chunk_scan_fused_kernel(Params p) {
     __shared__ __align__(16) char hb[P * SH];  // h_{c-1} in bf16, rows p
     // Tables of a block; two objects, so that one block's are read while
     // wave 0 writes the next block's.
-    __shared__ __align__(16) float tb0[kTbSize], tb1[kTbSize];
+    __shared__ __align__(16) float tb0[Cf::TB_SIZE], tb1[Cf::TB_SIZE];
 
     const int H = p.nheads, G = p.ngroups, HPG = p.heads_per_group;
     const int PF = p.headdim, PS = PF / P;  // channels of a head, items per head
@@ -229,16 +238,21 @@ void chunk_scan_fused_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int il = lane & 15, grp = lane >> 4;
-    const int tile = wide_tile<kWaves>(wave), md = tile >> 1;
-    // Waves meet md off-diagonal blocks each, so a block lasts as long as the
-    // waves with the most; issue priority grows with md so that the others
-    // fill the gaps.
-    if (md >= 3)
-        __builtin_amdgcn_s_setprio(3);
-    else if (md == 2)
-        __builtin_amdgcn_s_setprio(2);
-    else if (md == 1)
-        __builtin_amdgcn_s_setprio(1);
+    const int tile = wide_tile<W>(wave), md = tile >> 1;
+    // With 16 waves in one workgroup per compute unit, waves meet md
+    // off-diagonal blocks each and a block lasts as long as the waves with
+    // the most: their issue priority grows with md, so that the others fill
+    // the gaps.  (With two workgroups per compute unit the other
+    // workgroup's waves fill them; there all waves keep one priority.)
+    if constexpr (W == 16) {
+        const int prio = md * 4 / NBLK;
+        if (prio >= 3)
+            __builtin_amdgcn_s_setprio(3);
+        else if (prio == 2)
+            __builtin_amdgcn_s_setprio(2);
+        else if (prio == 1)
+            __builtin_amdgcn_s_setprio(1);
+    }
     const int nw = wave % Cf::WPN, pw = wave / Cf::WPN;  // the wave's state tiles
 
     const uint32_t HP2 = (uint32_t)H * PF * 2, GN2 = (uint32_t)G * N * 2;  // bytes per token row
@@ -305,22 +319,24 @@ void chunk_scan_fused_kernel(Params p) {
         for (int ks = 0; ks < KS; ++ks)
             cf[ks].v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, vc, 64 * ks, 0));
     };
-    // dt of a step's tokens 2 lane and 2 lane + 1 (0 past the sequence),
-    // which wave 0 turns into tables; loaded by every wave so that the value
-    // is not a branch result.  Issued first at a switch, so that waiting for
-    // these two loads never waits for the others.
-    float dtr0, dtr1;
+    // dt of a step's tokens TPL lane .. TPL lane + TPL - 1 (0 past the
+    // sequence), which wave 0 turns into tables.  Every wave issues the
+    // loads (so that the value is not a branch result), but only wave 0's
+    // descriptor covers any bytes.  Issued first at a switch, so that
+    // waiting for them never waits for the others.
+    float dtr[TPL];
     auto load_dt = [&](const Step &st, bool on) __attribute__((always_inline)) {
-        const auto r = dt_rows(st, on);
+        const auto r = dt_rows(st, on && wave == 0);
         int ln = lane;  // opaque: recomputed here
         asm volatile("" : "+v"(ln));
-        const uint32_t o = (uint32_t)(2 * ln) * H * 4;
-        dtr0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
-        dtr1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o + H * 4, 0, 0));
+        const uint32_t o = (uint32_t)(TPL * ln) * H * 4;
+#pragma unroll
+        for (int v = 0; v < TPL; ++v)
+            dtr[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o + v * H * 4, 0, 0));
     };
-    // Wave 0: the tables of a step from its dt values (dtr0, dtr1).
-    // Prefix sums in fp64 (a wave-wide scan on the DPP row shifts and
-    // broadcasts), each table entry rounded once.
+    // Wave 0: the tables of a step from its dt values (dtr).  Prefix sums
+    // in fp64 (within the lane, then a wave-wide scan of the lane totals on
+    // the DPP row shifts and broadcasts), each table entry rounded once.
     auto make_tables = [&](const Step &st, float *tb) __attribute__((always_inline)) {
         const int Qc = block_len(st.c);
         const double a = (double)((const __attribute__((address_space(4))) float *)(uintptr_t)p.A)[st.h];
@@ -328,11 +344,15 @@ void chunk_scan_fused_kernel(Params p) {
         // and not kept (or spilled) across the loop.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int i0 = 2 * ln;
-        const float d0 = dtr0, d1 = dtr1;
-        double s0 = (double)d0, s1 = s0 + (double)d1;
-        // inclusive scan of the lane totals s1
-        double tot = s1;
+        const int i0 = TPL * ln;
+        double sv[TPL];
+        double run = 0.0;
+#pragma unroll
+        for (int v = 0; v < TPL; ++v) {
+            run += (double)dtr[v];
+            sv[v] = run;
+        }
+        double tot = run;
         auto dpp_add = [&](auto ctrl, auto rmask) __attribute__((always_inline)) {
             constexpr int C = decltype(ctrl)::value, M = decltype(rmask)::value;
             const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(tot), C, M, 0xf, true);
@@ -345,36 +365,48 @@ void chunk_scan_fused_kernel(Params p) {
         dpp_add(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});  // row_shr:8
         dpp_add(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});  // row_bcast:15
         dpp_add(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});  // row_bcast:31
-        const double before = tot - s1;
-        s0 += before;
-        s1 += before;
-        // Sums at the ends of the 32-token blocks, e(m) = min(32m + 31, Qc - 1)
-        // (uniform lanes, read from their registers).
-        double se[kNBlk];
+        const double before = tot - run;
 #pragma unroll
-        for (int m = 0; m < kNBlk; ++m) {
+        for (int v = 0; v < TPL; ++v) sv[v] += before;
+        // Sums at the ends of the 32-token blocks, e(m) = min(32m + 31, Qc - 1)
+        // (uniform lanes and slots, read from their registers).
+        double se[NBLK];
+#pragma unroll
+        for (int m = 0; m < NBLK; ++m) {
             const int e = min(kStep * m + kStep - 1, Qc - 1);
-            const double v = (e & 1) ? s1 : s0;
-            se[m] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), e >> 1),
-                                     __builtin_amdgcn_readlane(__double2loint(v), e >> 1));
+            double v = sv[0];
+#pragma unroll
+            for (int k = 1; k < TPL; ++k) v = e % TPL == k ? sv[k] : v;
+            se[m] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), e / TPL),
+                                     __builtin_amdgcn_readlane(__double2loint(v), e / TPL));
         }
-        const int mb = ln >> 4;  // the lane's 32-token block
-        const double sl = mb == 0 ? se[0] : mb == 1 ? se[1] : mb == 2 ? se[2] : se[3];
-        const bool in0 = i0 < Qc, in1 = i0 + 1 < Qc;
-        const float c0 = (float)(a * s0 * kLog2eD), c1 = (float)(a * s1 * kLog2eD);
-        *reinterpret_cast<float2 *>(tb + kTbCs2 + i0) = float2{c0, c1};
-        *reinterpret_cast<float2 *>(tb + kTbCt + i0) =
-            float2{in0 ? c0 - log2f(d0) : __builtin_inff(), in1 ? c1 - log2f(d1) : __builtin_inff()};
-        *reinterpret_cast<float2 *>(tb + kTbDte + i0) =
-            float2{in0 ? d0 * exp_neg((float)(a * (sl - s0))) : 0.f, in1 ? d1 * exp_neg((float)(a * (sl - s1))) : 0.f};
-        // Per 32-token block m (lane m < 4): cs2 at e(m) and the Horner factor
-        // exp(cs_e(m) - cs_e(m-1)) (exp(cs_e(0)) for m = 0).
-        if (ln < kNBlk) {
-            const int m = ln;
-            const double sm = m == 0 ? se[0] : m == 1 ? se[1] : m == 2 ? se[2] : se[3];
-            const double sp = m == 0 ? 0.0 : m == 1 ? se[0] : m == 2 ? se[1] : se[2];
-            tb[kTbCe + m] = (float)(a * sm * kLog2eD);
-            tb[kTbG + m] = exp_neg((float)(a * (sm - sp)));
+        const int mb = i0 / kStep;  // the lane's 32-token block
+        double sl = se[0];
+#pragma unroll
+        for (int m = 1; m < NBLK; ++m) sl = mb == m ? se[m] : sl;
+        typedef float FV __attribute__((ext_vector_type(TPL)));
+        FV c, ct, de;
+#pragma unroll
+        for (int v = 0; v < TPL; ++v) {
+            const bool in = i0 + v < Qc;
+            c[v] = (float)(a * sv[v] * kLog2eD);
+            ct[v] = in ? c[v] - log2f(dtr[v]) : __builtin_inff();
+            de[v] = in ? dtr[v] * exp_neg((float)(a * (sl - sv[v]))) : 0.f;
+        }
+        *reinterpret_cast<FV *>(tb + TB_CS2 + i0) = c;
+        *reinterpret_cast<FV *>(tb + TB_CT + i0) = ct;
+        *reinterpret_cast<FV *>(tb + TB_DTE + i0) = de;
+        // Per 32-token block m (lane m < NBLK): cs2 at e(m) and the Horner
+        // factor exp(cs_e(m) - cs_e(m-1)) (exp(cs_e(0)) for m = 0).
+        if (ln < NBLK) {
+            double sm = se[0], sp = 0.0;
+#pragma unroll
+            for (int m = 1; m < NBLK; ++m) {
+                sm = ln == m ? se[m] : sm;
+                sp = ln == m ? se[m - 1] : sp;
+            }
+            tb[TB_CE + ln] = (float)(a * sm * kLog2eD);
+            tb[TB_G + ln] = exp_neg((float)(a * (sm - sp)));
         }
     };
 
@@ -472,8 +504,8 @@ void chunk_scan_fused_kernel(Params p) {
     };
 
     // ---- per-block factors (uniform).
-    float ce[kNBlk];   // cs2 at the end of each 32-token block
-    float gst[kNBlk];  // state Horner factors
+    float ce[NBLK];   // cs2 at the end of each 32-token block
+    float gst[NBLK];  // state Horner factors
     int Qc = 0, nblk = 0;
     bool live = false, full = false;
 
@@ -501,9 +533,9 @@ void chunk_scan_fused_kernel(Params p) {
                 }
         }
 #pragma unroll
-        for (int m = 0; m < kNBlk; ++m) {
-            ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[kTbCe + m])));
-            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[kTbG + m])));
+        for (int m = 0; m < NBLK; ++m) {
+            ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[TB_CE + m])));
+            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[TB_G + m])));
         }
     };
 
@@ -511,7 +543,7 @@ void chunk_scan_fused_kernel(Params p) {
     auto outputs = [&](const Step &st, const float *tb, f32x4 (&acc)[PT]) __attribute__((always_inline)) {
         const float dh = dh_of(st);
         const bool has_prev = st.c > 0 || p.init_state != nullptr;
-        const float cs2i = tb[kTbCs2 + 16 * tile + il];
+        const float cs2i = tb[TB_CS2 + 16 * tile + il];
         // Blue: exp(cs_i) C_i . h_{c-1} (rows p, column i).
         if (has_prev) {
 #pragma unroll
@@ -532,12 +564,12 @@ void chunk_scan_fused_kernel(Params p) {
         };
         // Orange below the diagonal block: G times exp2(cs2_i - cs2_e(m)) dte_j,
         // rounded to bf16 once, on raw x.
-        static_for<kNBlk - 1>([&](auto mc) __attribute__((always_inline)) {
+        static_for<NBLK - 1>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
             if (m >= md) return;
             const float ai = exp2_hw(cs2i - ce[m]);
             f32x4 w0, w1;
-            slot_pair(tb + kTbDte, m, w0, w1);
+            slot_pair(tb + TB_DTE, m, w0, w1);
             Frag<T> gf;
             const f32x4 g0 = g_half(m, 0);
 #pragma unroll
@@ -558,7 +590,7 @@ void chunk_scan_fused_kernel(Params p) {
             int di = 16 * (tile & 1) + il - 4 * grp;
             asm volatile("" : "+v"(di));
             f32x4 ct0, ct1;
-            slot_pair(tb + kTbCt, md, ct0, ct1);
+            slot_pair(tb + TB_CT, md, ct0, ct1);
             Frag<T> lf;
             const f32x4 g0 = g_half(md, 0);
 #pragma unroll
@@ -616,21 +648,21 @@ void chunk_scan_fused_kernel(Params p) {
         }
     };
 
-    // One step (tables in tb): the state (and the state after the accepted
-    // index if it lies in the step), then the outputs if the step is full.
-    // The state part comes first so that its products cover the latency of
-    // the C rows, fetched at the switch into the step; the y stores come
-    // last, and nothing waits for them.
+    // One step (tables in tb): the outputs if the step is full, (wave 0) the
+    // next step's tables, then the state (and the state after the accepted
+    // index if it lies in the step).  The next step's C rows are fetched
+    // before the state part, which covers their latency.
     auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
         __attribute__((always_inline)) {
-        // Wave 0: the next step's tables first (its dt values were fetched at
-        // the switch into this step), at top issue priority, so that they
-        // are never waited for.
-        if (has_next && wave == 0) {
-            __builtin_amdgcn_s_setprio(3);
-            make_tables(nx, tb_next);
-            __builtin_amdgcn_s_setprio(0);
+        {
+            f32x4 acc[PT];
+#pragma unroll
+            for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (live) outputs(st, tb, acc);
+            store_y(st, live, acc);
         }
+        if (has_next && wave == 0) make_tables(nx, tb_next);
+        load_c(nx, has_next && nx.c >= nx.c0);
         // Accepted index j in this step: its 32-token block mj and its
         // position jl in the step (uniform; -1 if not here).
         int jl = -1;
@@ -644,7 +676,7 @@ void chunk_scan_fused_kernel(Params p) {
         // j: the state at the end of the previous 32-token block times
         // exp(cs_j - cs_e(mj-1)) plus the tokens s <= j of block mj with
         // their exact factors exp2(cs2_j - ct_s), stored to state_out.
-        static_for<kNBlk>([&](auto mc) __attribute__((always_inline)) {
+        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
             if (m >= nblk) return;
             Frag<T> fa[NTW], fb[PTW];
@@ -653,12 +685,12 @@ void chunk_scan_fused_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < PTW; ++q) fb[q] = read_tr(xs + xS + kStep * m * SX + 32 * q, 16 * SX);
             if (m == mj) {
-                const float cs2j = tb[kTbCs2 + jl];
+                const float cs2j = tb[TB_CS2 + jl];
                 const float ej = exp2_hw(m == 0 ? cs2j : cs2j - ce[m > 0 ? m - 1 : 0]);
                 int j4 = jl - 4 * grp;  // slot r of half 0 is token 32m + 4grp + r
                 asm volatile("" : "+v"(j4));
                 f32x4 c0, c1, w0, w1;
-                slot_pair(tb + kTbCt, m, c0, c1);
+                slot_pair(tb + TB_CT, m, c0, c1);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     w0[r] = kStep * m + r > j4 ? 0.f : exp2_hw(cs2j - c0[r]);
@@ -668,21 +700,21 @@ void chunk_scan_fused_kernel(Params p) {
                 state_offsets(so);
                 float *dst = p.state_out + (int64_t)st.item * P * N;
 #pragma unroll
-                for (int q = 0; q < PTW; ++q) {
-                    Frag<T> fw = fb[q];
+                for (int a = 0; a < NTW; ++a) {
+                    Frag<T> fw = fa[a];
                     scale_frag(fw, w0, w1);
 #pragma unroll
-                    for (int a = 0; a < NTW; ++a) {
+                    for (int q = 0; q < PTW; ++q) {
                         f32x4 hv = hs[a][q] * ej;
-                        mma(fa[a], fw, hv);
+                        mma(fw, fb[q], hv);
                         *reinterpret_cast<f32x4 *>(dst + so[a][q]) = hv;
                     }
                 }
             }
             f32x4 w0, w1;
-            slot_pair(tb + kTbDte, m, w0, w1);
+            slot_pair(tb + TB_DTE, m, w0, w1);
 #pragma unroll
-            for (int q = 0; q < PTW; ++q) scale_frag(fb[q], w0, w1);
+            for (int a = 0; a < NTW; ++a) scale_frag(fa[a], w0, w1);
 #pragma unroll
             for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -691,13 +723,6 @@ void chunk_scan_fused_kernel(Params p) {
                     mma(fa[a], fb[q], hs[a][q]);
                 }
         });
-        {
-            f32x4 acc[PT];
-#pragma unroll
-            for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (live) outputs(st, tb, acc);
-            store_y(st, live, acc);
-        }
     };
 
     // ---- prologue: the first step's inputs and tables.  The tables of
@@ -707,17 +732,15 @@ void chunk_scan_fused_kernel(Params p) {
     load_dt(cur, true);
     load_x(cur, true);
     load_b(cur, true);
+    load_c(cur, cur.c >= cur.c0);
     wait_vmcnt<0>();
     if (wave == 0) make_tables(cur, tb0);
     lds_barrier();  // the tables are written
     begin_unit(cur);
     enter(cur, tb0);
     {
-        // In this order: what the step needs soonest is fetched first, since
-        // a wave's vector memory operations complete in issue order.
         const Step nx = nsteps > 1 ? next_step(cur) : cur;
         load_dt(nx, nsteps > 1);
-        load_c(cur, cur.c >= cur.c0);
         load_x(nx, nsteps > 1);
         load_b(nx, nsteps > 1);
     }
@@ -730,9 +753,9 @@ void chunk_scan_fused_kernel(Params p) {
         float *tbc = (s & 1) ? tb1 : tb0, *tbn = (s & 1) ? tb0 : tb1;
         compute(cur, has_next, nx, tbc, tbn);
         // Wait for the next step's x and B rows, not for this step's y
-        // stores issued after them: a wave's vector memory operations
-        // complete in the order they were issued.
-        wait_vmcnt<PT / 2>();
+        // stores or the next step's C rows issued after them: a wave's vector
+        // memory operations complete in the order they were issued.
+        wait_vmcnt<KS + PT / 2>();
         if (cur.c + 1 == cur.c1) end_unit(cur);
         if (has_next) {
             lds_barrier();  // every wave has finished this step's LDS reads; next tables written
@@ -740,8 +763,7 @@ void chunk_scan_fused_kernel(Params p) {
             enter(nx, tbn);
             const bool more = s + 2 < nsteps;
             const Step nn = more ? next_step(nx) : nx;
-            load_dt(nn, more);
-            load_c(nx, nx.c >= nx.c0);
+            load_dt(nn, more);  // first: see load_dt
             load_x(nn, more);
             load_b(nn, more);
             lds_barrier();
@@ -750,25 +772,36 @@ void chunk_scan_fused_kernel(Params p) {
     }
 }
 
-template <int NT, int PT>
+template <int NT, int PT, int QB>
 hipError_t launch_cfg(const Params &p, hipStream_t stream) {
-    using Cf = FusedCfg<NT, PT>;
+    using Cf = FusedCfg<NT, PT, QB>;
     if constexpr (!Cf::OK) {
         return hipErrorNotSupported;
     } else {
-        // Two workgroups per compute unit (each under half a CU's LDS).
-        const int grid = 2 * compute_units();
-        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+        const int grid = Cf::WGS_PER_CU * compute_units();
+        hipLaunchKernelGGL((chunk_scan_fused_kernel<NT, PT, QB>), dim3((unsigned)grid), dim3(Cf::THREADS), 0, stream,
+                           p);
         return hipGetLastError();
     }
+}
+
+// The block length: 256 tokens with one 16-wave workgroup per compute unit
+// where that geometry exists, else 128 tokens with two 8-wave workgroups.
+template <int NT, int PT>
+hipError_t launch_q(const Params &p, hipStream_t stream) {
+#ifndef SSD_FUSED_Q
+#define SSD_FUSED_Q 128
+#endif
+    if constexpr (SSD_FUSED_Q == 256 && FusedCfg<NT, PT, 256>::OK) return launch_cfg<NT, PT, 256>(p, stream);
+    else return launch_cfg<NT, PT, 128>(p, stream);
 }
 
 template <int NT>
 hipError_t dispatch_p(const Params &p, hipStream_t stream) {
     switch (p.headdim) {
-        case 32: return launch_cfg<NT, 2>(p, stream);
-        case 64: return launch_cfg<NT, 4>(p, stream);
-        case 128: return launch_cfg<NT, 4>(p, stream);  // two 64-channel items per head
+        case 32: return launch_q<NT, 2>(p, stream);
+        case 64: return launch_q<NT, 4>(p, stream);
+        case 128: return launch_q<NT, 4>(p, stream);  // two 64-channel items per head
         default: return hipErrorNotSupported;
     }
 }
@@ -780,7 +813,7 @@ bool chunk_scan_fused_takes(const Params &p) {
     // 32-bit byte offsets of one block's rows of x and y.
     const int64_t row_bytes = (int64_t)p.nheads * p.headdim * 2;
     return items >= kFusedMinItems && items < ((int64_t)1 << 30) && p.seqlen >= 1 &&
-           row_bytes * kQ < ((int64_t)1 << 31) && (int64_t)p.ngroups * p.dstate * 2 * kQ < ((int64_t)1 << 31) &&
+           row_bytes * 256 < ((int64_t)1 << 31) && (int64_t)p.ngroups * p.dstate * 2 * 256 < ((int64_t)1 << 31) &&
            (p.dstate == 64 || p.dstate == 128) && (p.headdim == 32 || p.headdim == 64 || p.headdim == 128);
 }
 
