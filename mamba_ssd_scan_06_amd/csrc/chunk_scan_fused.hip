@@ -112,10 +112,9 @@ struct FusedCfg {
     // the end of each 32-token block and the Horner factors.
     static constexpr int TB_CS2 = 0, TB_CT = Q, TB_DTE = 2 * Q, TB_CE = 3 * Q, TB_G = 3 * Q + NBLK;
     static constexpr int TB_SIZE = 3 * Q + 2 * NBLK;
-    // LDS rows are padded by 32 bytes: 16 lanes reading 16 bytes of 16
-    // consecutive rows, and the transposing reads of 4 consecutive rows,
-    // then spread over the banks, and every fragment address is one
-    // per-lane base plus an immediate offset.
+    // LDS rows are padded by 32 bytes, so that every fragment address is one
+    // per-lane base plus an immediate offset, and consecutive rows start on
+    // different banks.  (A 16-byte pad measured twice the bank conflicts.)
     static constexpr int SB = N * 2 + 32, SX = P * 2 + 32, SH = N * 2 + 32;  // bytes per LDS row of B, x, h
     static constexpr size_t LDS_BYTES = (size_t)Q * SB + (size_t)Q * SX + (size_t)P * SH + 2 * TB_SIZE * 4;
     // Two workgroups per compute unit when two fit its 160 KB of LDS.
