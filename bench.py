@@ -3,26 +3,33 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step is one full forward (chunk cumsum, chunk states, state passing,
-chunk outputs with the state-to-output term and D skip, and the state at the
-accepted index where the workload asks for it) over one batch of seeded
-synthetic inputs already resident in HBM.  The headline workload is the
-Mamba-2 2.7B layer shape (b=8, T=2048, H=80, P=64, N=128, G=1, Q=256, bf16
-in, fp32 state); the other four workloads are timed too and reported under
-"workloads".  Prints ONE JSON line.
+One step is one full forward over one batch of seeded synthetic inputs
+already resident in HBM: y with the D skip, the final state, and the state
+at the accepted index where the workload asks for it.  The headline workload
+is the Mamba-2 2.7B layer shape (b=8, T=2048, H=80, P=64, N=128, G=1, Q=256,
+bf16 in, fp32 state, zero initial state); the other four workloads are timed
+too and reported under "workloads".  Prints ONE JSON line.
 
-Per-kernel durations are measured live with HIP events that the library
-records between its kernels (ssd_chunk_scan_fwd_marked) on the stream the
-kernels run on, over the timed steps.  The roofline entry is for the kernel
-with the largest average duration; its algorithmic bytes and flops per
-launch are computed below from the problem sizes.  HBM traffic comes from
-the rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/ when it was
-taken on the current kernel source (else null).
+Timing has one source: HIP events recorded on the stream the library's
+kernels run on (torch's current stream, which the binding passes down), one
+before every step and one after the last.  "value" and "ms_per_step" are the
+K steps back to back (warm: whatever the 256 MB last-level cache keeps
+between steps).  The cold figures time single steps, each after a 512 MiB
+buffer is written on the same stream, which evicts the caches.
+
+The roofline entry is for the dominant kernel.  On the automatic path the
+headline step is ONE kernel (the single pass), so its average launch
+duration is the warm mean per step.  Its algorithmic bytes are the step's
+minimal HBM traffic: x and y, B and C, dt, the final state (and the initial
+state / state at index where present), each once.  Measured HBM traffic
+comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/
+when that was taken on the current kernel source (else null).
 
 Other modes:
-    --copy-probe            also run a plain 256 MiB device copy (counter calibration)
-    --summarize-pmc F W     turn two rocprofv3 --pmc output dirs into a profiles/ summary
-    --summarize-stats D     turn a rocprofv3 --kernel-trace --stats dir into a profiles/ summary
+    --copy-probe          also run a plain 256 MiB device copy (counter calibration)
+    --path P              time a given path (auto, one_chunk, single_pass, chunk_parallel)
+    --summarize-pmc D...  turn rocprofv3 --pmc output dirs into profiles/ summaries
+    --summarize-stats D   turn a rocprofv3 --kernel-trace --stats dir into a profiles/ summary
 """
 from __future__ import annotations
 
@@ -53,7 +60,8 @@ KERNEL_SOURCES = {
     "state_pass": ["state_pass.hip", "device_common.hpp"],
     "chunk_output": ["chunk_output_heads.hip", "chunk_output.hip", "device_common.hpp"],
     "chunk_scan_fused": ["chunk_scan_fused.hip", "device_common.hpp"],
-    "state_at_index": ["chunk_state.hip", "device_common.hpp"],
+    "one_chunk": ["one_chunk.hip", "device_common.hpp"],
+    "empty_sequence": ["state_pass.hip"],
 }
 CSRC = os.path.join(ROOT, "mamba_ssd_scan_06_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -65,55 +73,45 @@ def chunk_lengths(wl):
     return [min(Q, T - c) for c in range(0, T, Q)]
 
 
-def algorithmic_work(wl, idx=None):
-    """Minimal HBM bytes and algorithmic flops of each kernel for one call.
+def step_bytes(wl):
+    """Minimal HBM bytes of one step: every input read once and every output
+    written once (x, y, B, C, dt, the final state, and the initial state and
+    the state at the accepted index where the workload has them)."""
+    b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    e = 2 if wl.dtype == "bf16" else 4
+    st = b * H * P * N * 4
+    return (2 * b * T * H * P * e + 2 * b * T * G * N * e + b * T * H * 4 + 2 * H * 4 + st
+            + (st if wl.init_state else 0) + (st + 4 * b if wl.state_out else 0))
 
-    Bytes count each tensor a kernel must read or write once: inputs in their
-    dtype, the per-token tables (cs, ct, dte) and chunk states in fp32, the
-    states entering each chunk in the input dtype.  Flops count the causal
-    triangle only and C.B^T once per (b, chunk, group), not per head."""
+
+def kernel_bytes(wl):
+    """Minimal HBM bytes of each chunk-parallel kernel on its own: the
+    tensors it must read or write once, including the workspace
+    intermediates it exchanges with the other kernels (cs, ct, dte and the
+    chunk states in fp32, the states entering each chunk in the input
+    dtype).  The single pass and one_chunk exchange nothing: their bytes are
+    the step's."""
     b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
     e = 2 if wl.dtype == "bf16" else 4
     nc = len(chunk_lengths(wl))
-    x = b * T * H * P * e
-    bc = b * T * G * N * e
-    dt = b * T * H * 4
-    tab = b * H * nc * wl.chunk * 4      # one per-token table
-    st = b * H * P * N * 4               # one fp32 state per (b, h)
-    S = nc * st                          # chunk states, fp32
-    prev_chunks = nc if wl.init_state else nc - 1
-    prev = prev_chunks * st // 4 * e     # states entering chunks, input dtype
-    qs = chunk_lengths(wl)
-    work = {
-        "chunk_cumsum": dict(bytes=dt + 3 * tab, flops=b * T * H),
-        "chunk_state": dict(bytes=x + bc + dt + tab + S, flops=2 * b * H * sum(qs) * N * P),
-        "state_pass": dict(bytes=S + prev + st + (st if wl.init_state else 0), flops=2 * b * nc * H * P * N),
-        "chunk_output": dict(
-            bytes=2 * x + 2 * bc + 3 * tab + prev,
-            flops=b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P for q in qs)
-            + 2 * b * H * N * P * sum(q for c, q in enumerate(qs) if c > 0 or wl.init_state)),
-    }
-    # single pass: x, B, C and the tables read once, y and the states written once
-    work["chunk_scan_fused"] = dict(
-        bytes=2 * x + 2 * bc + 3 * tab + (st if wl.init_state else 0) + st + (st if wl.state_out else 0),
-        flops=work["chunk_state"]["flops"] + work["chunk_output"]["flops"])
-    if 1 <= T <= 32 and nc == 1:
-        # one fused kernel: h0 read once, both states written once
-        toks = [min(j, T - 1) + 1 if j >= 0 else 0 for j in (idx if idx is not None else [])] if wl.state_out else []
-        work["one_chunk"] = dict(
-            bytes=2 * x + 2 * bc + dt + (st if wl.init_state else 0) + st + (st if wl.state_out else 0),
-            flops=b * (G * T * (T + 1) * N + H * T * (T + 1) * P) + 4 * b * H * P * N * T
-            + 2 * H * P * N * sum(toks))
-    if wl.state_out:
-        Q = wl.chunk
-        toks = [(j % Q) + 1 if j >= 0 else 0 for j in (idx if idx is not None else [])]
-        work["state_at_index"] = dict(
-            bytes=sum(t * (H * P * e + G * N * e + H * 4) for t in toks) + b * H * Q * 4 + 2 * st,
-            flops=2 * H * N * P * sum(toks))
-    return work
+    x, bc, dt = b * T * H * P * e, b * T * G * N * e, b * T * H * 4
+    tab = b * H * nc * wl.chunk * 4
+    st = b * H * P * N * 4
+    S = nc * st
+    prev = (nc if wl.init_state else nc - 1) * st // 4 * e
+    out = {"chunk_cumsum": dt + 3 * tab,
+           "chunk_state": x + bc + dt + tab + S,
+           "state_pass": S + prev + st + (st if wl.init_state else 0),
+           "chunk_output": 2 * x + 2 * bc + 3 * tab + prev,
+           "chunk_scan_fused": step_bytes(wl), "one_chunk": step_bytes(wl)}
+    return out
 
 
 def total_flops(wl):
+    """Algorithmic flops of one step of the block decomposition at the
+    workload's chunk size: per chunk of q tokens, C.B^T over the causal
+    triangle once per group, the masked product with x per head, the chunk
+    state and the state-to-output product per head."""
     qs = chunk_lengths(wl)
     b, H, P, N, G = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
     return b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P + 4 * H * q * N * P for q in qs)
@@ -125,40 +123,6 @@ def source_hash(kernel):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
-
-
-# ------------------------------------------------------------- HIP events
-class HipEvents:
-    """hipEventCreate / hipEventElapsedTime through the HIP runtime torch loaded."""
-
-    def __init__(self):
-        import torch  # noqa: F401  (torch's runtime is the one libssd binds to)
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-
-    def create(self, n):
-        out = []
-        for _ in range(n):
-            ev = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(ev))
-            if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
-            out.append(ev.value)
-        return out
-
-    def elapsed_ms(self, a, b):
-        ms = ctypes.c_float()
-        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        if rc != 0:
-            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-        return ms.value
-
-    def destroy(self, evs):
-        for e in evs:
-            self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
 # ------------------------------------------------------------------ running
@@ -178,8 +142,18 @@ def device_inputs(inp, device):
                 state_out_idx=t(inp.state_out_idx))
 
 
-def time_workload(wl, steps, warmup, device, events):
-    """Returns (inputs, result dict) for `steps` timed forwards of `wl`."""
+def _stats(us):
+    s = sorted(us)
+    return {"mean_us": round(sum(s) / len(s), 2), "median_us": round(s[len(s) // 2], 2), "min_us": round(s[0], 2),
+            "max_us": round(s[-1], 2), "steps": len(s)}
+
+
+FLUSH_BYTES = 512 << 20
+
+
+def time_workload(wl, steps, warmup, device, path_name="auto", cold_steps=10):
+    """Times `steps` forwards of `wl` back to back (warm) and `cold_steps`
+    single forwards after a cache flush.  Returns (inputs, result dict)."""
     import torch
 
     import mamba_ssd_scan_06_amd as ssd
@@ -189,62 +163,65 @@ def time_workload(wl, steps, warmup, device, events):
     b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
     code = ssd.SSD_DTYPE_BF16 if wl.dtype == "bf16" else ssd.SSD_DTYPE_F32
     shape = ssd.make_shape(b, T, H, P, N, G)
-    ws = torch.empty(ssd.ssd_workspace_bytes(shape, wl.chunk, code), dtype=torch.uint8, device=device)
+    path = {v: k for k, v in ssd.PATH_NAMES.items()}[path_name]
+    run_path = path if path != ssd.SSD_PATH_AUTO else ssd.ssd_select_path(shape, wl.chunk, code)
+    ws_bytes = ssd.ssd_get_workspace_layout(shape, wl.chunk, code).total_bytes \
+        if run_path == ssd.SSD_PATH_CHUNK_PARALLEL else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
     y = torch.empty_like(dev["x"])
     fin = torch.empty((b, H, P, N), dtype=torch.float32, device=device)
     sout = torch.empty_like(fin) if wl.state_out else None
     args = (dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], dev["init_state"], wl.chunk,
             dev["state_out_idx"])
-    kw = dict(y=y, final_state=fin, state_out=sout, workspace=ws)
+    kw = dict(y=y, final_state=fin, state_out=sout, workspace=ws, path=path)
+    # The kernels one step launches (one untimed call with marks).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for m in marks:
+        m.record()
+    *_, names = ssd.ssd_chunk_scan_fwd_ex(*args, marks=[m.cuda_event for m in marks], **kw)
     for _ in range(warmup):
-        ssd.ssd_chunk_scan_fwd(*args, **kw)
-    # Whole steps, back to back, with events only around the timed region.
+        ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Warm: K steps back to back, an event before each and after the last.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
-        ssd.ssd_chunk_scan_fwd(*args, **kw)
-    end.record()
+    evs[0].record()
+    for k in range(steps):
+        ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
+        evs[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / steps
-    # Per-kernel durations: the same steps again, with HIP events recorded on
-    # the kernels' stream between kernels.
-    nk = 5 if wl.state_out else 4
-    marks = [events.create(nk + 1) for _ in range(steps)]
-    names = None
-    for k in range(steps):
-        _, _, _, names = ssd.ssd_chunk_scan_fwd_marked(*args, marks=marks[k], **kw)
+    warm_us = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)]
+    ms_step = evs[0].elapsed_time(evs[steps]) / steps
+    # Cold: each step after 512 MiB are written on the same stream.
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cold_steps)]
+    for k, (e0, e1) in enumerate(pairs):
+        flush.fill_(float(k))
+        e0.record()
+        ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
+        e1.record()
     torch.cuda.synchronize()
-    per_kernel = {}
-    for i, name in enumerate(names):
-        per_kernel[name] = sum(events.elapsed_ms(m[i], m[i + 1]) for m in marks) / steps
-    for m in marks:
-        events.destroy(m)
-    return inp, dict(ms_per_step=ms_step, wall_s=wall, kernel_ms=per_kernel, kernel_order=names)
-
-
-def roofline_entry(wl, name, ms, work, traffic):
-    w = work[name]
-    ai = w["flops"] / w["bytes"]
-    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if ai >= ridge:
-        achieved = w["flops"] / (ms * 1e-3) / 1e12
-        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
-                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4), "traffic": traffic,
-                "alg_bytes": w["bytes"], "alg_flops": w["flops"], "avg_ms": round(ms, 5)}
-    achieved = w["bytes"] / (ms * 1e-3) / 1e9
-    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "alg_bytes": w["bytes"],
-            "alg_flops": w["flops"], "avg_ms": round(ms, 5)}
+    cold_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+    del flush
+    return inp, dict(ms_per_step=ms_step, wall_s=wall, warm=_stats(warm_us), cold=_stats(cold_us),
+                     kernels=names, path=ssd.PATH_NAMES[run_path])
 
 
 def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch from profiles/<kernel>_<workload>_hbm_traffic.txt, if
+    """HBM bytes per launch from profiles/<kernel>_<workload>_counters.txt, if
     the counters were taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
+    vals = read_profile(kernel, workload)
+    if vals is None or vals.get("kernel_source_sha256") != source_hash(kernel):
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def read_profile(kernel, workload):
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -253,12 +230,31 @@ def traffic_from_profile(kernel, workload):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != source_hash(kernel):
-        return None
-    try:
-        return int(float(vals["traffic_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+    return vals
+
+
+def roofline_entry(wl, res):
+    """Roofline of the dominant kernel.  A one-kernel step's kernel is timed
+    by the step's events; for a step of several kernels the entry covers the
+    whole step (named as such)."""
+    ms = res["ms_per_step"]
+    names = res["kernels"]
+    kernel = names[0] if len(names) == 1 else "step (" + " + ".join(names) + ")"
+    alg_bytes = step_bytes(wl)
+    flops = total_flops(wl)
+    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    ai = flops / alg_bytes
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = traffic_from_profile(names[0], wl.name) if len(names) == 1 else None
+    common = {"kernel": kernel, "traffic": traffic, "alg_bytes": alg_bytes, "alg_flops": flops,
+              "avg_launch_us": round(ms * 1e3, 2), "arith_intensity": round(ai, 1), "ridge": round(ridge, 1)}
+    if ai >= ridge:
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_flops, 4), **common}
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), **common}
 
 
 # Single-token decode at the 2.7B-layer shape: the state updated in place.
@@ -294,17 +290,39 @@ def time_decode(steps, warmup, device):
             "state_GB/s": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(wl, inp):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, seqs=None):
+    """The fp64 oracle on the host cores, on the first `seqs` sequences of the
+    workload (all heads, all tokens; default all of them): once on one
+    thread, once on every core this process may use."""
     import oracle
 
     cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state, inp.state_out_idx,
-                       nthreads=cores)
-    dt = time.perf_counter() - t0
-    return {"value": round(wl.tokens / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full {wl.name} workload ({wl.tokens} tokens), fp64 recurrence, one pass, "
-                      f"{dt:.2f} s wall on {cores} threads"}
+    n = min(seqs or wl.batch, wl.batch)
+    sl = lambda a: None if a is None else a[:n]
+    sample = (sl(inp.x), sl(inp.dt), inp.A, sl(inp.B), sl(inp.C), inp.D, sl(inp.init_state), sl(inp.state_out_idx))
+    tokens = n * wl.seqlen
+    runs = {}
+    for threads in (1, cores):
+        t0 = time.perf_counter()
+        oracle.ssd_forward(*sample, nthreads=threads)
+        runs[threads] = time.perf_counter() - t0
+    return {"value": round(tokens / runs[cores], 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {n} of {wl.batch} sequences of {wl.name} ({tokens} tokens, all {wl.nheads} "
+                      f"heads), fp64 recurrence, one pass: {runs[cores]:.2f} s on {cores} threads, "
+                      f"{runs[1]:.2f} s on 1",
+            "one_core": {"value": round(tokens / runs[1], 1), "unit": "tokens/s", "cores": 1},
+            "cpu_model": cpu_model()}
 
 
 def copy_probe(device):
@@ -334,7 +352,6 @@ def summarize_stats(d, workload=HEADLINE, command=""):
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     lines = [f"# rocprofv3 kernel-trace statistics, workload {workload}", f"# command: {command}",
-             f"# source: {', '.join(os.path.relpath(f, ROOT) for f in files)}",
              "# name | calls | total_ns | avg_ns | min_ns | max_ns | pct"]
     for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
         name = r.get("Name", "")
@@ -347,57 +364,99 @@ def summarize_stats(d, workload=HEADLINE, command=""):
     print(out)
 
 
-def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
-    def per_kernel(d, counter):
+KERNEL_KEYS = ("chunk_scan_fused", "one_chunk", "chunk_output", "chunk_state", "state_pass", "chunk_cumsum",
+               "empty_sequence")
+# fp32 inputs run v_mfma_f32_16x16x4_f32 (2048 flops), bf16 v_mfma_f32_16x16x32_bf16 (16384).
+MFMA_FLOPS = {"bf16": 16384, "f32": 2048}
+N_SIMDS, N_SE = 1024, 32
+
+
+def _kernel_key(symbol):
+    """The step a kernel symbol belongs to (the state at index runs the generic
+    chunk_state kernel and is counted with it)."""
+    for key in KERNEL_KEYS:
+        if re.search(rf"(?<![a-z_]){key}(_heads|_dma)?_kernel", symbol):
+            return key
+    return None
+
+
+def summarize_pmc(dirs, workload=HEADLINE, commands=()):
+    """Per kernel of one workload: the median per dispatch of every counter
+    found under `dirs` (rows of one dispatch summed), FETCH_SIZE / WRITE_SIZE
+    turned into bytes with the copy probe's factor, and the derived figures."""
+    per = {}   # kernel key -> counter -> dispatch -> value
+    symbols = {}
+    for d in dirs:
         _, rows = _read_csv(os.path.join(d, "**", "*counter_collection.csv"))
-        vals = {}
         for r in rows:
-            if r.get("Counter_Name") != counter:
+            sym = r.get("Kernel_Name", "")
+            key = "copy" if "copy" in sym.lower() else _kernel_key(sym)
+            if key is None:
                 continue
-            vals.setdefault(r.get("Kernel_Name", ""), []).append(float(r.get("Counter_Value", 0)))
-        return vals
+            symbols.setdefault(key, sym)
+            disp = (d, int(r.get("Dispatch_Id") or 0))
+            c = per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+            c[disp] = c.get(disp, 0.0) + float(r["Counter_Value"])
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
-    copy_bytes = 256 << 20
+    def med(key, counter):
+        vals = sorted(per.get(key, {}).get(counter, {}).values())
+        return vals[len(vals) // 2] if vals else None
 
-    def find(d, key):
-        # kernel symbols look like "...chunk_output_heads_kernel<8, 4, 16, true>(...)"; the
-        # step's kernel is the matching one with the most dispatches
-        pat = re.compile(rf"(?<![a-z_]){re.escape(key)}(_heads|_dma)?_kernel") if key != "copy" else None
-        hits = {k: v for k, v in d.items() if (pat.search(k) if pat else key in k)}
-        return max(hits.items(), key=lambda kv: len(kv[1])) if hits else (None, None)
-
-    _, cf = find(fetch, "copy")
-    _, cw = find(write, "copy")
-    if not cf or not cw:
-        raise SystemExit("copy probe kernel not found in counter output")
-    f_copy = copy_bytes / (sorted(cf)[len(cf) // 2] * 1024.0)
-    w_copy = copy_bytes / (sorted(cw)[len(cw) // 2] * 1024.0)
     wl = ssd_inputs.WORKLOADS[workload]
-    work = algorithmic_work(wl)
-    for kernel in ("chunk_scan_fused", "chunk_output", "chunk_state", "state_pass", "chunk_cumsum"):
-        kf_name, kf = find(fetch, kernel)
-        _, kw = find(write, kernel)
-        if not kf or not kw:
+    copy_bytes = 256 << 20
+    # The copy probe runs last: its three 256 MiB copies are the last three
+    # copy dispatches of each run (earlier ones upload the inputs).
+    def copy_factor(counter):
+        disp = per.get("copy", {}).get(counter, {})
+        last = {}
+        for (d, i), v in disp.items():
+            last.setdefault(d, []).append((i, v))
+        vals = sorted(v for runs in last.values() for _, v in sorted(runs)[-3:])
+        return copy_bytes / (vals[len(vals) // 2] * 1024.0) if vals else None
+
+    fc, wc = copy_factor("FETCH_SIZE"), copy_factor("WRITE_SIZE")
+    kb = kernel_bytes(wl)
+    for key in per:
+        if key == "copy":
             continue
-        fb = sorted(kf)[len(kf) // 2] * 1024.0 * f_copy
-        wb = sorted(kw)[len(kw) // 2] * 1024.0 * w_copy
-        out = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
+        c = {k: med(key, k) for k in per[key]}
+        sym = symbols[key]
+        lines = [f"# rocprofv3 --pmc counters of {key} on {workload} (medians per dispatch; a dispatch's rows summed)",
+                 f"# kernel symbol: {sym[:sym.rfind('(')] if sym.endswith(')') else sym}"]
+        lines += [f"# command: {cmd}" for cmd in commands]
+        lines += [f"kernel_source_sha256 = {source_hash(key)}"]
+        for k in sorted(c):
+            lines.append(f"{k} = {c[k]:.0f}")
+        ab = kb.get(key)
+        if c.get("FETCH_SIZE") is not None and c.get("WRITE_SIZE") is not None and fc and wc:
+            fb, wb = c["FETCH_SIZE"] * 1024.0 * fc, c["WRITE_SIZE"] * 1024.0 * wc
+            lines += ["# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by 256 MiB over what",
+                      "# the same counter reads for a plain 256 MiB device copy in the same run",
+                      f"copy_factor_fetch = {fc:.4f}", f"copy_factor_write = {wc:.4f}",
+                      f"fetch_bytes_per_launch = {fb:.0f}", f"write_bytes_per_launch = {wb:.0f}",
+                      f"traffic_bytes_per_launch = {fb + wb:.0f}"]
+            if ab:
+                lines += [f"algorithmic_bytes_per_launch = {ab}", f"traffic_over_algorithmic = {(fb + wb) / ab:.3f}"]
+        if c.get("SQ_INSTS_MFMA") is not None:
+            ex = c["SQ_INSTS_MFMA"] * MFMA_FLOPS[wl.dtype]
+            lines += [f"# executed MFMA flops = SQ_INSTS_MFMA x {MFMA_FLOPS[wl.dtype]} flops per instruction",
+                      f"mfma_flops_executed = {ex:.0f}"]
+            if key in ("chunk_scan_fused", "one_chunk"):
+                alg = total_flops(wl)
+                lines += [f"algorithmic_flops_per_launch = {alg}", f"executed_over_algorithmic = {ex / alg:.3f}"]
+        if c.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None and c.get("SQ_BUSY_CYCLES"):
+            # SQ_BUSY_CYCLES sums the 32 shader engines; the MFMA busy counter sums the 1024 SIMDs.
+            se_cycles = c["SQ_BUSY_CYCLES"] / N_SE
+            lines += ["# MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x SQ_BUSY_CYCLES / 32 SEs)",
+                      f"mfma_busy_frac = {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMDS * se_cycles):.4f}"]
+        if c.get("SQ_WAIT_ANY") is not None and c.get("SQ_WAVE_CYCLES"):
+            lines.append(f"wait_any_over_wave_cycles = {c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:.4f}")
+        if c.get("SQ_LDS_BANK_CONFLICT") is not None and c.get("SQ_ACTIVE_INST_LDS"):
+            lines.append(f"lds_bank_conflict_over_active_lds = "
+                         f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_ACTIVE_INST_LDS']:.4f}")
+        out = os.path.join(PROFILES, f"{key}_{workload}_counters.txt")
         with open(out, "w") as f:
-            f.write(f"# HBM traffic of {kernel} on {workload} from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE\n")
-            f.write(f"# command: {command}\n")
-            f.write(f"# kernel symbol: {kf_name[:kf_name.rfind('(')] if kf_name.endswith(')') else kf_name}\n")
-            f.write("# counters are KiB per dispatch; each is scaled by (256 MiB / what the same counter reads\n")
-            f.write("# for a plain 256 MiB device copy in the same run); medians over dispatches\n")
-            f.write(f"kernel_source_sha256 = {source_hash(kernel)}\n")
-            f.write(f"copy_factor_fetch = {f_copy:.4f}\n")
-            f.write(f"copy_factor_write = {w_copy:.4f}\n")
-            f.write(f"fetch_bytes_per_launch = {fb:.0f}\n")
-            f.write(f"write_bytes_per_launch = {wb:.0f}\n")
-            f.write(f"traffic_bytes_per_launch = {fb + wb:.0f}\n")
-            f.write(f"algorithmic_bytes_per_launch = {work[kernel]['bytes']}\n")
-            f.write(f"traffic_over_algorithmic = {(fb + wb) / work[kernel]['bytes']:.3f}\n")
+            f.write("\n".join(lines) + "\n")
         print(out)
 
 
@@ -405,21 +464,24 @@ def summarize_pmc(fetch_dir, write_dir, workload=HEADLINE, command=""):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # ~0.2 s of untimed steps: the GPU's clocks ramp up over the first milliseconds.
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--cold-steps", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=list(ssd_inputs.WORKLOADS))
-    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--path", default="auto", choices=["auto", "one_chunk", "single_pass", "chunk_parallel"])
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads and the decode line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-stats", metavar="DIR")
-    ap.add_argument("--command", default="", help="command line recorded in a profile summary")
+    ap.add_argument("--command", action="append", default=[], help="command line recorded in a profile summary")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc, workload=args.workload, command=args.command)
+        return summarize_pmc(args.summarize_pmc, workload=args.workload, commands=args.command)
     if args.summarize_stats:
-        return summarize_stats(args.summarize_stats, workload=args.workload, command=args.command)
+        return summarize_stats(args.summarize_stats, workload=args.workload, command=" ".join(args.command))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SSD forward here runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
@@ -431,23 +493,12 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    events = HipEvents()
 
     wl = ssd_inputs.WORKLOADS[args.workload]
-    inp, res = time_workload(wl, args.steps, args.warmup, device, events)
-    work = algorithmic_work(wl, inp.state_out_idx)
+    inp, res = time_workload(wl, args.steps, args.warmup, device, args.path, args.cold_steps)
     ms = res["ms_per_step"]
     flops = total_flops(wl)
     tflops = flops / (ms * 1e-3) / 1e12
-    dominant = max(res["kernel_ms"], key=res["kernel_ms"].get)
-    roof = roofline_entry(wl, dominant, res["kernel_ms"][dominant], work,
-                          traffic_from_profile(dominant, wl.name))
-    kernels = {}
-    for name, kms in res["kernel_ms"].items():
-        w = work.get(name, {"bytes": 0, "flops": 0})
-        kernels[name] = {"avg_us": round(kms * 1e3, 2), "alg_bytes": w["bytes"], "alg_flops": w["flops"],
-                         "GB/s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1),
-                         "TFLOP/s": round(w["flops"] / (kms * 1e-3) / 1e12, 2)}
 
     workloads = {}
     if not args.headline_only:
@@ -455,15 +506,14 @@ def main():
             if name == wl.name:
                 continue
             w2 = ssd_inputs.WORKLOADS[name]
-            inp2, r2 = time_workload(w2, max(10, args.steps // 4), max(3, args.warmup // 2), device, events)
+            _, r2 = time_workload(w2, max(10, args.steps // 4), max(10, args.warmup // 4), device, "auto", 5)
             m2 = r2["ms_per_step"]
-            work2 = algorithmic_work(w2, inp2.state_out_idx)
-            workloads[name] = {"ms_per_step": round(m2, 5), "tokens_per_s": round(w2.tokens / (m2 * 1e-3), 1),
+            workloads[name] = {"path": r2["path"], "kernels": r2["kernels"], "ms_per_step": round(m2, 5),
+                               "tokens_per_s": round(w2.tokens / (m2 * 1e-3), 1),
                                "TFLOP/s": round(total_flops(w2) / (m2 * 1e-3) / 1e12, 2),
-                               "alg_GB/s": round(sum(work2[k]["bytes"] for k in r2["kernel_ms"]) / (m2 * 1e-3) / 1e9,
-                                                 1),
-                               "kernel_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
-            del inp2
+                               "step_bytes": step_bytes(w2),
+                               "hbm_frac": round(step_bytes(w2) / (m2 * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                               "warm": r2["warm"], "cold": r2["cold"]}
 
     decode = None if args.headline_only else time_decode(max(20, args.steps // 2), 5, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, inp)
@@ -482,13 +532,16 @@ def main():
         "data": "synthetic (seeded counter-based generator; inputs resident in HBM)",
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen": wl.seqlen, "nheads": wl.nheads,
                    "headdim": wl.headdim, "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk": wl.chunk,
-                   "parallelism": "single GPU"},
+                   "path": res["path"], "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "alg_flops_per_step": flops,
-        "roofline": roof,
+        "timing": {"source": "HIP events on the library's stream, one before each step and one after the last",
+                   "warm": res["warm"], "cold": dict(res["cold"], flush_bytes=FLUSH_BYTES),
+                   "wall_s": round(res["wall_s"], 4)},
+        "roofline": roofline_entry(wl, res),
         "cpu_baseline": cpu,
-        "kernels": kernels,
+        "kernels": res["kernels"],
         "workloads": workloads,
         "decode": decode,
         "input_sha256": inp.sha256,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -71,11 +71,14 @@ typedef enum {
     SSD_ERR_SHAPE = 2,       /* a size is negative, or ngroups does not divide nheads */
     SSD_ERR_CHUNK = 3,       /* chunk_size not in {8, 16, 32, 64, 128, 256}          */
     SSD_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned              */
-    SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than ssd_workspace_bytes   */
+    SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the call's path needs */
     SSD_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
-    SSD_ERR_ARGS = 7,        /* state_out given without state_out_idx or vice versa  */
+    SSD_ERR_ARGS = 7,        /* state_out without state_out_idx or vice versa, an unknown
+                                dtype or path, or marks missing for n_marks > 0      */
     SSD_ERR_HIP = 8,         /* a kernel launch failed; outputs are unspecified      */
-    SSD_ERR_UNSUPPORTED = 9  /* headdim not in {16,32,64,128} or dstate not in {16,32,64,128,256} */
+    SSD_ERR_UNSUPPORTED = 9  /* headdim not in {16,32,64,128}, dstate not in {16,32,64,128,256},
+                                fp32 with headdim*dstate > 16384, or a requested path
+                                that does not take the call                          */
 } ssd_status;
 
 /* Problem sizes.  batch and seqlen may be 0. */
@@ -88,17 +91,47 @@ typedef struct {
     int64_t ngroups;  /* G: B/C groups; head h reads group h*G/H      */
 } ssd_shape;
 
-/* Where the intermediates live inside the workspace after a call (byte
- * offsets from the workspace pointer).  Exposed so that the individual steps
- * can be checked.  A call whose tokens fit one chunk and number at most 32
- * is computed by one fused kernel and leaves the workspace untouched.  bf16
- * calls with dstate 64 or 128, headdim 32, 64 or 128, chunk_size 128 or 256
- * and at least 256 items (an item is a (b, h) pair, or a 64-channel half of
- * a head of headdim 128) run the single-pass kernel after the cumsum: it
- * fills cumsum, ct, dt_decay, block_decay, sync and (with state_out) hj,
- * uses only hand-off entries of states and leaves prev unwritten.  Every
- * other call runs the chunk-parallel kernels, which fill every region (sync
- * is only cleared).
+/* How a call is computed.  Every path gives the same results up to
+ * floating-point rounding; the automatic choice depends only on the shape,
+ * chunk_size and dtype (ssd_select_path).
+ *   SSD_PATH_ONE_CHUNK       at most 32 tokens in one chunk (the multi-step
+ *                            verify, a decode step): one kernel reads the
+ *                            initial state once and writes y, final_state
+ *                            and state_out.  Needs headdim a multiple of
+ *                            1024 / dstate.
+ *   SSD_PATH_SINGLE_PASS     bf16, dstate 64 or 128, headdim 32, 64 or 128,
+ *                            at least 64 items (an item is a (b, h) pair, or
+ *                            a 64-channel half of a head of headdim 128):
+ *                            one kernel walks each item's sequence in
+ *                            128-token blocks with the state in registers
+ *                            (the state passing of section
+ *                            "深入解析分块与状态传递机制" of the "Transformers
+ *                            are SSMs" article, carried inside the kernel).
+ *                            When there are fewer items than workgroups, an
+ *                            item's blocks are split into ranges; a range
+ *                            not starting at token 0 first recomputes the
+ *                            state it starts from, so no workgroup ever
+ *                            waits for another.  Its internal block length
+ *                            does not depend on chunk_size.
+ *   SSD_PATH_CHUNK_PARALLEL  any call: the four steps of the block
+ *                            decomposition as separate kernels, with the
+ *                            intermediates in the workspace.
+ * No path uses the workspace except SSD_PATH_CHUNK_PARALLEL. */
+typedef enum {
+    SSD_PATH_AUTO = 0,
+    SSD_PATH_ONE_CHUNK = 1,
+    SSD_PATH_SINGLE_PASS = 2,
+    SSD_PATH_CHUNK_PARALLEL = 3
+} ssd_path;
+
+/* The path ssd_chunk_scan_fwd takes for this problem; SSD_PATH_AUTO (0) when
+ * batch or seqlen is 0 (no kernel but a state copy runs), -1 when the
+ * arguments are invalid (ssd_last_error() says why). */
+int ssd_select_path(const ssd_shape *shape, int chunk_size, ssd_dtype dtype);
+
+/* The workspace of SSD_PATH_CHUNK_PARALLEL: byte offsets from the workspace
+ * pointer of the intermediates that path leaves there, exposed so that the
+ * individual steps can be checked.
  *   cumsum   fp32 [batch, nheads, nchunks, chunk_size]: the chunk-local
  *            cumulative log-decay A[h] * sum_{k<=i} dt[b, c*Q+k, h]; tokens
  *            past seqlen count as dt = 0.
@@ -106,45 +139,34 @@ typedef struct {
  *            so that dt_j exp(cs_i - cs_j) = exp2(cs_i log2(e) - ct_j).
  *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
  *            (within seqlen) of the 32-token block holding i.
- *   block_decay fp32 [batch, nheads, nchunks, 16]: for the chunk's 32-token
- *            blocks m = 0..7, entry m is cs * log2(e) at the block's last
- *            token e(m) and entry 8+m is exp(cs_e(m) - cs_e(m-1))
- *            (exp(cs_e(0)) for m = 0); blocks past the chunk repeat its
- *            last token.
  *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: entry c is the
  *            state chunk c reaches from a zero initial state.
  *   prev     dtype, same layout: entry c is the state entering chunk c,
  *            rounded to nearest even to dtype; entry 0 is written only when
- *            init_state is given (otherwise it is zero and left unwritten).
+ *            init_state is given (otherwise it is never read).
  *   hj       fp32 [batch, nheads, headdim, dstate]: the state entering the
  *            chunk that holds state_out_idx[b] (written only with state_out).
- *   sync     int32 [2 + 2*batch*nheads]: a time-out word (nonzero if a wait of
- *            the single-pass kernel for a state handed over by another
- *            workgroup gave up, which only a fault elsewhere can cause;
- *            outputs are then unspecified) and two hand-off flags per
- *            (b, h) (one per half of the channels when headdim 128 is
- *            split in two); cleared by the first kernel of each call.  The
- *            single-pass kernel hands a state over through the states region
- *            (entry [b, 0, h], the half's rows) when it splits a sequence's
- *            chunks between two workgroups. */
+ * Every region a kernel reads was written earlier in the same call: the
+ * contents on entry never matter. */
 typedef struct {
     size_t cumsum_offset;
     size_t ct_offset;
     size_t dt_decay_offset;
-    size_t block_decay_offset;
     size_t states_offset;
     size_t prev_offset;
     size_t hj_offset;
-    size_t sync_offset;
-    size_t total_bytes;
+    size_t total_bytes;   /* bytes SSD_PATH_CHUNK_PARALLEL needs (0 when batch or seqlen is 0) */
     int64_t nchunks;
 } ssd_workspace_layout;
 
-/* Bytes of device workspace ssd_chunk_scan_fwd needs for this problem
- * (0 when the arguments are invalid; ssd_last_error() says why). */
+/* Bytes of device workspace ssd_chunk_scan_fwd needs for this problem: the
+ * layout's total_bytes when the call takes SSD_PATH_CHUNK_PARALLEL, else 0
+ * (then workspace may be NULL).  0 also when the arguments are invalid
+ * (ssd_last_error() says why). */
 size_t ssd_workspace_bytes(const ssd_shape *shape, int chunk_size, ssd_dtype dtype);
 
-/* Fills *out with the workspace layout for this problem. */
+/* Fills *out with the workspace layout of SSD_PATH_CHUNK_PARALLEL for this
+ * problem (also for problems that take another path automatically). */
 ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_dtype dtype,
                                     ssd_workspace_layout *out);
 
@@ -168,12 +190,15 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
  *                                       non-NULL exactly when state_out_idx is
  *   shape, dtype             sizes and element type as above
  *   workspace     device scratch of at least ssd_workspace_bytes(...) bytes,
- *                 16-byte aligned; contents on entry are ignored
+ *                 16-byte aligned; contents on entry are ignored; may be
+ *                 NULL when ssd_workspace_bytes(...) is 0
  *   hip_stream    hipStream_t as void*, NULL for the default stream
  *
  * Outputs must not overlap inputs, each other or the workspace, with one
  * exception: final_state may be init_state itself (same pointer), updating
- * the state in place (a decode step, a verifier keeping its cache).
+ * the state in place (a decode step, a verifier keeping its cache).  An
+ * in-place call on SSD_PATH_SINGLE_PASS runs every item whole on one
+ * workgroup (no ranges), since a range's recomputation reads init_state.
  * Errors: see ssd_status; checks are host-side and happen before any launch. */
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const void *B, const void *C, const float *D,
@@ -183,24 +208,30 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const ssd_shape *shape, ssd_dtype dtype,
                               void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* Same as ssd_chunk_scan_fwd, and additionally records caller-created HIP
- * events (hipEvent_t passed as void*) on hip_stream around the kernels, so
- * that a caller can time each kernel in place:
- *   marks[0]  before the first kernel,
- *   marks[k]  after the k-th kernel launched (k = 1 .. n_marks-1).
+/* Same as ssd_chunk_scan_fwd with two additions.
+ *   path    SSD_PATH_AUTO, or the path to take (SSD_ERR_UNSUPPORTED when it
+ *           does not take the call; calls of zero tokens or sequences only
+ *           copy states whatever the path).  The workspace must then hold the
+ *           bytes that path needs: the layout's total_bytes for
+ *           SSD_PATH_CHUNK_PARALLEL, none for the others.
+ *   marks   caller-created HIP events (hipEvent_t as void*) recorded on
+ *           hip_stream around the kernels, so that a caller can time each
+ *           kernel in place: marks[0] before the first kernel, marks[k]
+ *           after the k-th kernel launched (k = 1 .. n_marks-1).  Marks
+ *           beyond the kernels launched are not recorded.  n_marks may be 0
+ *           (marks NULL).
  * On SSD_OK, *n_kernels (if non-NULL) is the number of kernels launched and
  * kernel_names[k-1] (if kernel_names is non-NULL and k < n_marks) names the
- * kernel that marks[k] ends.  Marks beyond the kernels launched are not
- * recorded.  Used by the benchmark to measure per-kernel durations. */
-ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float *A,
-                                     const void *B, const void *C, const float *D,
-                                     const float *init_state, int chunk_size,
-                                     void *y, float *final_state,
-                                     const int32_t *state_out_idx, float *state_out,
-                                     const ssd_shape *shape, ssd_dtype dtype,
-                                     void *workspace, size_t workspace_bytes, void *hip_stream,
-                                     void *const *marks, int n_marks, int *n_kernels,
-                                     const char **kernel_names);
+ * kernel that marks[k] ends. */
+ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
+                                 const void *B, const void *C, const float *D,
+                                 const float *init_state, int chunk_size,
+                                 void *y, float *final_state,
+                                 const int32_t *state_out_idx, float *state_out,
+                                 const ssd_shape *shape, ssd_dtype dtype,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream,
+                                 int path, void *const *marks, int n_marks, int *n_kernels,
+                                 const char **kernel_names);
 
 /* Static description of a status code. */
 const char *ssd_status_string(ssd_status status);

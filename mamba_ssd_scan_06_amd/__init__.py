@@ -15,8 +15,9 @@ import os
 
 __all__ = [
     "SsdError", "ssd_abi_version", "ssd_status_string", "ssd_last_error", "ssd_workspace_bytes",
-    "ssd_get_workspace_layout", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_marked", "workspace_views",
-    "library_path",
+    "ssd_get_workspace_layout", "ssd_select_path", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_ex",
+    "workspace_views", "library_path", "SSD_PATH_AUTO", "SSD_PATH_ONE_CHUNK", "SSD_PATH_SINGLE_PASS",
+    "SSD_PATH_CHUNK_PARALLEL",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +26,12 @@ _lib = None
 
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_BF16 = 1
+SSD_PATH_AUTO = 0
+SSD_PATH_ONE_CHUNK = 1
+SSD_PATH_SINGLE_PASS = 2
+SSD_PATH_CHUNK_PARALLEL = 3
+PATH_NAMES = {SSD_PATH_AUTO: "auto", SSD_PATH_ONE_CHUNK: "one_chunk", SSD_PATH_SINGLE_PASS: "single_pass",
+              SSD_PATH_CHUNK_PARALLEL: "chunk_parallel"}
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_CHUNK", 4: "SSD_ERR_ALIGN",
           5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_ARGS", 8: "SSD_ERR_HIP",
           9: "SSD_ERR_UNSUPPORTED"}
@@ -37,11 +44,9 @@ class ssd_shape(ctypes.Structure):
 
 class ssd_workspace_layout(ctypes.Structure):
     _fields_ = [("cumsum_offset", ctypes.c_size_t), ("ct_offset", ctypes.c_size_t),
-                ("dt_decay_offset", ctypes.c_size_t), ("block_decay_offset", ctypes.c_size_t),
-                ("states_offset", ctypes.c_size_t),
+                ("dt_decay_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
                 ("prev_offset", ctypes.c_size_t), ("hj_offset", ctypes.c_size_t),
-                ("sync_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
-                ("nchunks", ctypes.c_int64)]
+                ("total_bytes", ctypes.c_size_t), ("nchunks", ctypes.c_int64)]
 
 
 class SsdError(RuntimeError):
@@ -72,12 +77,14 @@ def _load():
     lib.ssd_workspace_bytes.restype = sz
     lib.ssd_get_workspace_layout.argtypes = [shp, i32, i32, ctypes.POINTER(ssd_workspace_layout)]
     lib.ssd_get_workspace_layout.restype = i32
+    lib.ssd_select_path.argtypes = [shp, i32, i32]
+    lib.ssd_select_path.restype = i32
     lib.ssd_chunk_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp, sz, vp]
     lib.ssd_chunk_scan_fwd.restype = i32
-    lib.ssd_chunk_scan_fwd_marked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp, sz, vp,
-                                              ctypes.POINTER(vp), i32, ctypes.POINTER(i32),
-                                              ctypes.POINTER(ctypes.c_char_p)]
-    lib.ssd_chunk_scan_fwd_marked.restype = i32
+    lib.ssd_chunk_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp, sz, vp,
+                                          i32, ctypes.POINTER(vp), i32, ctypes.POINTER(i32),
+                                          ctypes.POINTER(ctypes.c_char_p)]
+    lib.ssd_chunk_scan_fwd_ex.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -119,6 +126,13 @@ def ssd_get_workspace_layout(shape: ssd_shape, chunk_size: int, dtype: int) -> s
     return out
 
 
+def ssd_select_path(shape: ssd_shape, chunk_size: int, dtype: int) -> int:
+    path = int(_load().ssd_select_path(ctypes.byref(shape), int(chunk_size), int(dtype)))
+    if path < 0:
+        raise SsdError(7, ssd_last_error())
+    return path
+
+
 def _dtype_code(torch, t) -> int:
     if t.dtype == torch.bfloat16:
         return SSD_DTYPE_BF16
@@ -138,65 +152,96 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, init_state=None, chunk_size: int 
 
     x [b,T,H,P] bf16|fp32, dt [b,T,H] fp32, A [H] fp32, B/C [b,T,G,N] like x,
     D [H] fp32 or None, init_state [b,H,P,N] fp32 or None, state_out_idx [b]
-    int32 or None.  Outputs are allocated when not given.  Returns
-    (y, final_state or None, state_out or None).  Raises SsdError on any
-    status other than SSD_OK.
+    int32 or None.  Outputs are allocated when not given; given ones must
+    have the exact shape, dtype and device.  Returns (y, final_state or None,
+    state_out or None).  Raises ValueError/TypeError for a tensor that does
+    not fit the call (before anything runs) and SsdError on any status other
+    than SSD_OK.
     """
     y, final_state, state_out, _ = _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state,
-                                        return_final_state, state_out, workspace, stream, None)
+                                        return_final_state, state_out, workspace, stream, SSD_PATH_AUTO, None)
     return y, final_state, state_out
 
 
-def ssd_chunk_scan_fwd_marked(x, dt, A, B, C, D=None, init_state=None, chunk_size: int = 256,
-                              state_out_idx=None, *, marks, y=None, final_state=None,
-                              return_final_state: bool = True, state_out=None, workspace=None, stream=None):
-    """ssd_chunk_scan_fwd that also records the HIP events `marks` (raw
-    hipEvent_t handles as ints): marks[0] before the first kernel, marks[k]
-    after the k-th.  Returns (y, final_state, state_out, kernel_names)."""
+def ssd_chunk_scan_fwd_ex(x, dt, A, B, C, D=None, init_state=None, chunk_size: int = 256, state_out_idx=None, *,
+                          path: int = SSD_PATH_AUTO, marks=(), y=None, final_state=None,
+                          return_final_state: bool = True, state_out=None, workspace=None, stream=None):
+    """ssd_chunk_scan_fwd on a chosen path (SSD_PATH_*), recording the HIP
+    events `marks` (raw hipEvent_t handles as ints): marks[0] before the
+    first kernel, marks[k] after the k-th.  Returns (y, final_state,
+    state_out, names of the kernels that marks[1:] end)."""
     return _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state, return_final_state,
-                state_out, workspace, stream, marks)
+                state_out, workspace, stream, int(path), list(marks))
+
+
+def _expect(name, t, shape, dtype, device):
+    """Checks one tensor argument; `shape` is the exact shape required."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, x on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state, return_final_state, state_out,
-         workspace, stream, marks):
+         workspace, stream, path, marks):
     import torch
 
-    lib = _load()
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be [b,T,H,P] and B, C [b,T,G,N]")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(torch, x)
-    for name, t, dtype in (("dt", dt, torch.float32), ("A", A, torch.float32), ("B", B, x.dtype),
-                           ("C", C, x.dtype), ("D", D, torch.float32), ("init_state", init_state, torch.float32),
-                           ("state_out_idx", state_out_idx, torch.int32)):
-        if t is None:
-            continue
-        if t.dtype != dtype:
-            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if t.device != x.device:
-            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    dev = x.device
+    state_shape = (b, H, P, N)
+    _expect("x", x, x.shape, x.dtype, dev)
+    _expect("B", B, (b, T, G, N), x.dtype, dev)
+    _expect("C", C, (b, T, G, N), x.dtype, dev)
+    _expect("dt", dt, (b, T, H), torch.float32, dev)
+    _expect("A", A, (H,), torch.float32, dev)
+    if D is not None:
+        _expect("D", D, (H,), torch.float32, dev)
+    if init_state is not None:
+        _expect("init_state", init_state, state_shape, torch.float32, dev)
+    if state_out_idx is not None:
+        _expect("state_out_idx", state_out_idx, (b,), torch.int32, dev)
+    elif state_out is not None:
+        raise ValueError("state_out needs state_out_idx")
+    if y is not None:
+        _expect("y", y, x.shape, x.dtype, dev)
+    if final_state is not None:
+        _expect("final_state", final_state, state_shape, torch.float32, dev)
+    if state_out is not None:
+        _expect("state_out", state_out, state_shape, torch.float32, dev)
+    if workspace is not None:
+        if workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        _expect("workspace", workspace, workspace.shape, torch.uint8, dev)
+    if not x.is_cuda:
+        raise ValueError(f"tensors must be on a GPU device, x is on {dev}")
+
+    lib = _load()
     shape = make_shape(b, T, H, P, N, G)
+    layout = ssd_get_workspace_layout(shape, chunk_size, code)  # raises the status of an invalid shape
+    chosen = ssd_select_path(shape, chunk_size, code)
+    run_path = path if path != SSD_PATH_AUTO and chosen != SSD_PATH_AUTO else chosen
+    ws_bytes = layout.total_bytes if run_path == SSD_PATH_CHUNK_PARALLEL else 0
     if y is None:
         y = torch.empty_like(x)
     if final_state is None and return_final_state:
-        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+        final_state = torch.empty(state_shape, dtype=torch.float32, device=dev)
     if state_out_idx is not None and state_out is None:
-        state_out = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
-    ws_bytes = ssd_workspace_bytes(shape, chunk_size, code)
-    if ws_bytes == 0 and b * T > 0:
-        raise SsdError(2, ssd_last_error())
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        state_out = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else None
+        stream = torch.cuda.current_stream(dev).cuda_stream
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), int(chunk_size), _ptr(y),
             _ptr(final_state), _ptr(state_out_idx), _ptr(state_out), ctypes.byref(shape), code, _ptr(workspace),
-            int(workspace.numel()), ctypes.c_void_p(stream) if stream else None)
+            int(workspace.numel()) if workspace is not None else 0, ctypes.c_void_p(stream) if stream else None)
     if marks is None:
         _check(lib.ssd_chunk_scan_fwd(*args))
         return y, final_state, state_out, None
@@ -204,15 +249,16 @@ def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_stat
     arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(m)) for m in marks])
     names = (ctypes.c_char_p * max(n, 1))()
     count = ctypes.c_int(0)
-    _check(lib.ssd_chunk_scan_fwd_marked(*args, arr, n, ctypes.byref(count), names))
+    _check(lib.ssd_chunk_scan_fwd_ex(*args, int(path), arr, n, ctypes.byref(count), names))
     used = min(count.value, n - 1) if n > 0 else 0
     return y, final_state, state_out, [names[k].decode() for k in range(used)]
 
 
 def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
-    """Views into a workspace after a call: cs [b,H,nc,Q] fp32, the chunk
-    states from a zero start [b,nc,H,P,N] fp32, and the states entering each
-    chunk [b,nc,H,P,N] in the input dtype (entry 0 only with init_state)."""
+    """Views into the chunk-parallel path's workspace after a call, by the
+    layout of include/ssd.h: cs, ct and dte [b,H,nc,Q] fp32, the chunk states
+    from a zero start [b,nc,H,P,N] fp32, and the states entering each chunk
+    [b,nc,H,P,N] in the input dtype (entry 0 only with init_state)."""
     import torch
 
     lay = ssd_get_workspace_layout(shape, chunk_size, dtype)
@@ -221,7 +267,13 @@ def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
     n_cs = b * H * nc * chunk_size
     n_st = b * nc * H * P * N
     tdt, esz = (torch.bfloat16, 2) if dtype == SSD_DTYPE_BF16 else (torch.float32, 4)
-    cs = workspace[lay.cumsum_offset:lay.cumsum_offset + 4 * n_cs].view(torch.float32).view(b, H, nc, chunk_size)
-    st = workspace[lay.states_offset:lay.states_offset + 4 * n_st].view(torch.float32).view(b, nc, H, P, N)
-    prev = workspace[lay.prev_offset:lay.prev_offset + esz * n_st].view(tdt).view(b, nc, H, P, N)
-    return cs, st, prev
+
+    def region(off, nbytes, dt, dims):
+        return workspace[off:off + nbytes].view(dt).view(*dims)
+
+    tab = (b, H, nc, chunk_size)
+    return dict(cs=region(lay.cumsum_offset, 4 * n_cs, torch.float32, tab),
+                ct=region(lay.ct_offset, 4 * n_cs, torch.float32, tab),
+                dte=region(lay.dt_decay_offset, 4 * n_cs, torch.float32, tab),
+                states=region(lay.states_offset, 4 * n_st, torch.float32, (b, nc, H, P, N)),
+                prev=region(lay.prev_offset, esz * n_st, tdt, (b, nc, H, P, N)))

@@ -9,13 +9,6 @@ namespace ssd {
 
 enum class Elem { F32, BF16 };
 
-constexpr int kBlkStride = 16;  // floats per (b, h, c) in the block-factor table
-constexpr int kSyncHeader = 2;  // words before the hand-off flags in the sync region
-// The single-pass kernel may split a head's channels p in two (headdim 128:
-// two independent 64-channel halves), so each (b, h) has two flags.
-constexpr int kFlagsPerHead = 2;
-inline int64_t sync_words(int64_t batch, int64_t nheads) { return kSyncHeader + kFlagsPerHead * batch * nheads; }
-
 // Everything a kernel needs, passed by value.  Pointers are device pointers
 // with the layouts documented in include/ssd.h; `cs` and `states` point into
 // the caller's workspace.
@@ -37,11 +30,6 @@ struct Params {
     float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
     float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
-    int *sync;                // workspace int32 [2 + b*H]: [0] unused, [1] wait time-out word, then one
-                              // hand-off flag per (b, h) of the single-pass kernel
-    float *blk;               // workspace [b,H,nc,kBlkStride] fp32: per 32-token block m of the chunk,
-                              // [m] = cs*log2(e) at the block's last token, [8+m] = exp(cs_e(m) - cs_e(m-1))
-                              // (exp(cs_e(0)) for m = 0)
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
@@ -72,8 +60,10 @@ constexpr int64_t kFusedMinItems = 64;
 bool chunk_scan_fused_takes(const Params &p);
 hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream);
 // Whole forward of a one-chunk call of at most 32 tokens in one kernel (y,
-// final_state, state_out; the workspace is not used).  Returns
-// hipErrorNotSupported for other calls and unsupported shapes.
+// final_state, state_out; the workspace is not used).  one_chunk_takes says
+// whether it takes a call; launch_one_chunk returns hipErrorNotSupported for
+// calls it does not take.
+bool one_chunk_takes(const Params &p);
 hipError_t launch_one_chunk(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_empty_sequence(const Params &p, hipStream_t stream);
 

@@ -238,10 +238,14 @@ hipError_t dispatch_n(const Params &p, hipStream_t stream) {
 
 }  // namespace
 
-bool one_chunk_applies(const Params &p) { return p.seqlen >= 1 && p.seqlen <= kMaxTokens && p.nchunks == 1; }
+// A pass over the state covers 256 threads / (dstate / 4) threads per row =
+// 1024 / dstate rows; headdim must be a multiple of it.
+bool one_chunk_takes(const Params &p) {
+    return p.seqlen >= 1 && p.seqlen <= kMaxTokens && p.nchunks == 1 && p.headdim % (1024 / p.dstate) == 0;
+}
 
 hipError_t launch_one_chunk(const Params &p, Elem e, hipStream_t stream) {
-    if (!one_chunk_applies(p)) return hipErrorNotSupported;
+    if (!one_chunk_takes(p)) return hipErrorNotSupported;
     return e == Elem::BF16 ? dispatch_n<bf16>(p, stream) : dispatch_n<float>(p, stream);
 }
 

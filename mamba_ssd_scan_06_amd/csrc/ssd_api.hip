@@ -1,17 +1,22 @@
-// Host side of libssd: argument checks, workspace layout and the launch
-// sequence of the SSD chunked-scan forward.  The public contract is
-// include/ssd.h.
+// Host side of libssd: argument checks, path choice, workspace layout and
+// the launch sequence of the SSD chunked-scan forward.  The public contract
+// is include/ssd.h.
 //
-// Launch sequence on the caller's stream (each step of the block
-// decomposition in section "SSD算法" of the "Transformers are SSMs" article):
-//   1. chunk_cumsum     dt, A            -> cs, ct, dte  (chunk-local log-decay tables)
-//   2. chunk_state      x, B, dt, cs     -> states[c]    (green: S_c from a zero start)
-//   3. state_pass       states, cs, h0   -> prev[c] = h_{c-1}, hj, final_state (yellow)
-//   4. chunk_output     x, B, C, cs, dt tables, prev, D -> y  (orange + blue + D skip)
-//   5. state_at_index   x, B, cs, dt, hj -> state_out  (only with state_out)
-// A call whose tokens fit one chunk of at most 32 tokens (the multi-step
-// verify) instead runs one fused kernel, one_chunk, which writes y,
-// final_state and state_out directly and leaves the workspace untouched.
+// Paths (one is chosen per call from the shape, chunk size and dtype; see
+// select_path):
+//   one_chunk        a call of at most 32 tokens in one chunk (the multi-step
+//                    verify): one kernel writes y, final_state and state_out.
+//   single pass      bf16, dstate 64/128, headdim 32/64/128, at least 64
+//                    items: chunk_scan_fused runs the whole forward with the
+//                    state carried in registers (no workspace).
+//   chunk parallel   everything else, each step of the block decomposition in
+//                    section "SSD算法" of the "Transformers are SSMs" article:
+//     1. chunk_cumsum     dt, A            -> cs, ct, dte  (chunk-local log-decay tables)
+//     2. chunk_state      x, B, dt, cs     -> states[c]    (green: S_c from a zero start)
+//     3. state_pass       states, cs, h0   -> prev[c] = h_{c-1}, hj, final_state (yellow)
+//     4. chunk_output     x, B, C, cs, dt tables, prev, D -> y  (orange + blue + D skip)
+//     5. state_at_index   x, B, cs, dt, hj -> state_out  (only with state_out)
+// A call of zero tokens copies init_state (or zeros) to the requested states.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -70,10 +75,11 @@ ssd_status check_shape(const ssd_shape *s, int chunk, ssd_dtype dtype) {
 }
 
 struct Layout {
-    size_t cs_off, ct_off, dte_off, blk_off, st_off, prev_off, hj_off, sync_off, total;
+    size_t cs_off, ct_off, dte_off, st_off, prev_off, hj_off, total;
     int64_t nc;
 };
 
+// Workspace of the chunk-parallel path.
 Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     Layout L;
     L.nc = (s->seqlen + chunk - 1) / chunk;
@@ -84,13 +90,43 @@ Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     L.cs_off = 0;
     L.ct_off = tab_bytes;
     L.dte_off = 2 * tab_bytes;
-    L.blk_off = 3 * tab_bytes;
-    L.st_off = L.blk_off + round_up((size_t)s->batch * s->nheads * L.nc * ssd::kBlkStride * sizeof(float));
+    L.st_off = 3 * tab_bytes;
     L.prev_off = L.st_off + round_up(n_st * sizeof(float));
     L.hj_off = L.prev_off + round_up(n_st * esz);
-    L.sync_off = L.hj_off + round_up(n_hj * sizeof(float));
-    L.total = L.nc > 0 ? L.sync_off + round_up((size_t)ssd::sync_words(s->batch, s->nheads) * sizeof(int32_t)) : 0;
+    L.total = L.nc > 0 && s->batch > 0 ? L.hj_off + round_up(n_hj * sizeof(float)) : 0;
     return L;
+}
+
+// Size fields of the kernel parameters (no pointers).
+ssd::Params shape_params(const ssd_shape *s, int chunk) {
+    ssd::Params p = {};
+    p.batch = s->batch;
+    p.seqlen = s->seqlen;
+    p.nheads = (int)s->nheads;
+    p.headdim = (int)s->headdim;
+    p.dstate = (int)s->dstate;
+    p.ngroups = (int)s->ngroups;
+    p.chunk = chunk;
+    p.nchunks = (int)((s->seqlen + chunk - 1) / chunk);
+    p.heads_per_group = (int)(s->nheads / s->ngroups);
+    return p;
+}
+
+// The path a call takes when none is asked for.  Shape checks have passed.
+ssd_path select_path(const ssd::Params &p, ssd_dtype dtype) {
+    if (p.batch == 0 || p.seqlen == 0) return SSD_PATH_AUTO;  // nothing to compute but state copies
+    if (ssd::one_chunk_takes(p)) return SSD_PATH_ONE_CHUNK;
+    if (dtype == SSD_DTYPE_BF16 && ssd::chunk_scan_fused_takes(p)) return SSD_PATH_SINGLE_PASS;
+    return SSD_PATH_CHUNK_PARALLEL;
+}
+
+bool path_takes(ssd_path path, const ssd::Params &p, ssd_dtype dtype) {
+    switch (path) {
+        case SSD_PATH_ONE_CHUNK: return ssd::one_chunk_takes(p);
+        case SSD_PATH_SINGLE_PASS: return dtype == SSD_DTYPE_BF16 && ssd::chunk_scan_fused_takes(p);
+        case SSD_PATH_CHUNK_PARALLEL: return true;
+        default: return false;
+    }
 }
 
 struct Range {
@@ -138,18 +174,6 @@ struct Launcher {
         if (err != hipSuccess) return;
         record(name, launch());
     }
-
-    // Like step, but a launcher answering hipErrorNotSupported (a call or
-    // shape it does not take, nothing enqueued) leaves no trace and makes
-    // it return false.
-    template <typename F>
-    bool try_step(const char *name, F &&launch) {
-        if (err != hipSuccess) return true;
-        const hipError_t r = launch();
-        if (r == hipErrorNotSupported) return false;
-        record(name, r);
-        return true;
-    }
 };
 
 }  // namespace
@@ -158,7 +182,13 @@ extern "C" {
 
 size_t ssd_workspace_bytes(const ssd_shape *shape, int chunk_size, ssd_dtype dtype) {
     if (check_shape(shape, chunk_size, dtype) != SSD_OK) return 0;
+    if (select_path(shape_params(shape, chunk_size), dtype) != SSD_PATH_CHUNK_PARALLEL) return 0;
     return layout_of(shape, chunk_size, dtype).total;
+}
+
+int ssd_select_path(const ssd_shape *shape, int chunk_size, ssd_dtype dtype) {
+    if (check_shape(shape, chunk_size, dtype) != SSD_OK) return -1;
+    return (int)select_path(shape_params(shape, chunk_size), dtype);
 }
 
 ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_dtype dtype,
@@ -170,22 +200,20 @@ ssd_status ssd_get_workspace_layout(const ssd_shape *shape, int chunk_size, ssd_
     out->cumsum_offset = L.cs_off;
     out->ct_offset = L.ct_off;
     out->dt_decay_offset = L.dte_off;
-    out->block_decay_offset = L.blk_off;
     out->states_offset = L.st_off;
     out->prev_offset = L.prev_off;
     out->hj_offset = L.hj_off;
-    out->sync_offset = L.sync_off;
     out->total_bytes = L.total;
     out->nchunks = L.nc;
     return SSD_OK;
 }
 
-ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float *A, const void *B,
-                                     const void *C, const float *D, const float *init_state, int chunk_size,
-                                     void *y, float *final_state, const int32_t *state_out_idx,
-                                     float *state_out, const ssd_shape *shape, ssd_dtype dtype, void *workspace,
-                                     size_t workspace_bytes, void *hip_stream, void *const *marks, int n_marks,
-                                     int *n_kernels, const char **kernel_names) {
+ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                                 const float *D, const float *init_state, int chunk_size, void *y,
+                                 float *final_state, const int32_t *state_out_idx, float *state_out,
+                                 const ssd_shape *shape, ssd_dtype dtype, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream, int path, void *const *marks, int n_marks, int *n_kernels,
+                                 const char **kernel_names) {
     if (n_marks < 0 || (n_marks > 0 && !marks)) return fail(SSD_ERR_ARGS, "marks must hold n_marks events");
     ssd_status st = check_shape(shape, chunk_size, dtype);
     if (st != SSD_OK) return st;
@@ -194,19 +222,33 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     if ((state_out == nullptr) != (state_out_idx == nullptr))
         return fail(SSD_ERR_ARGS, "state_out and state_out_idx must be given together");
 
+    ssd::Params p = shape_params(shape, chunk_size);
+    const ssd_path chosen = select_path(p, dtype);
+    ssd_path run_path = chosen;
+    if (path != SSD_PATH_AUTO) {
+        if (path != SSD_PATH_ONE_CHUNK && path != SSD_PATH_SINGLE_PASS && path != SSD_PATH_CHUNK_PARALLEL)
+            return fail(SSD_ERR_ARGS, "unknown path %d", path);
+        // Zero-token and zero-batch calls only copy states, whatever the path.
+        if (chosen != SSD_PATH_AUTO) {
+            if (!path_takes((ssd_path)path, p, dtype))
+                return fail(SSD_ERR_UNSUPPORTED, "path %d does not take this call", path);
+            run_path = (ssd_path)path;
+        }
+    }
+
     const size_t esz = dtype == SSD_DTYPE_BF16 ? 2 : 4;
     const size_t n_tok = (size_t)b * T;
     const size_t x_bytes = n_tok * H * P * esz, bc_bytes = n_tok * G * N * esz;
     const size_t dt_bytes = n_tok * H * sizeof(float), state_bytes = (size_t)b * H * P * N * sizeof(float);
     const Layout L = layout_of(shape, chunk_size, dtype);
+    const size_t ws_need = run_path == SSD_PATH_CHUNK_PARALLEL ? L.total : 0;
 
     if (n_tok > 0) {
         if (!x || !dt || !A || !B || !C || !y) return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
-        if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
-        if (workspace_bytes < L.total)
-            return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+        if (ws_need > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+        if (workspace_bytes < ws_need)
+            return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, ws_need);
     }
-    if (b > 0 && state_out_idx == nullptr && state_out != nullptr) return fail(SSD_ERR_ARGS, "state_out_idx missing");
 
     const void *aligned16[] = {x, B, C, y, init_state, final_state, state_out, workspace};
     const char *names16[] = {"x", "B", "C", "y", "init_state", "final_state", "state_out", "workspace"};
@@ -223,7 +265,7 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
                             range("B", B, bc_bytes), range("C", C, bc_bytes), range("D", D, H * sizeof(float)),
                             range("init_state", init_state, state_bytes),
                             range("state_out_idx", state_out_idx, b * sizeof(int32_t)),
-                            range("workspace", workspace, L.total)};
+                            range("workspace", workspace, ws_need)};
     // final_state may be init_state itself (an in-place update, e.g. decode):
     // every kernel reads each initial-state element before that element is
     // written, in the same thread, and reads it nowhere else.
@@ -237,9 +279,9 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
             if (overlaps(outs[i], outs[k])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[k].name);
     }
 
+    if (n_kernels) *n_kernels = 0;
     if (b == 0 || (T == 0 && !final_state && !state_out)) return SSD_OK;  // nothing to enqueue
 
-    ssd::Params p;
     p.x = x;
     p.dt = dt;
     p.A = A;
@@ -251,24 +293,13 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     p.y = y;
     p.final_state = final_state;
     p.state_out = state_out;
-    char *ws = static_cast<char *>(workspace);
+    char *ws = run_path == SSD_PATH_CHUNK_PARALLEL ? static_cast<char *>(workspace) : nullptr;
     p.cs = ws ? reinterpret_cast<float *>(ws + L.cs_off) : nullptr;
     p.ct = ws ? reinterpret_cast<float *>(ws + L.ct_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
-    p.blk = ws ? reinterpret_cast<float *>(ws + L.blk_off) : nullptr;
-    p.sync = ws ? reinterpret_cast<int *>(ws + L.sync_off) : nullptr;
     p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
     p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;
     p.hj = ws && state_out ? reinterpret_cast<float *>(ws + L.hj_off) : nullptr;
-    p.batch = b;
-    p.seqlen = T;
-    p.nheads = (int)H;
-    p.headdim = (int)P;
-    p.dstate = (int)N;
-    p.ngroups = (int)G;
-    p.chunk = chunk_size;
-    p.nchunks = (int)L.nc;
-    p.heads_per_group = (int)(H / G);
     p.no_split = in_place ? 1 : 0;
     const ssd::Elem e = dtype == SSD_DTYPE_BF16 ? ssd::Elem::BF16 : ssd::Elem::F32;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -278,12 +309,11 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
     if (n_marks > 0) run.err = hipEventRecord(static_cast<hipEvent_t>(marks[0]), stream);
     if (T == 0) {
         run.step("empty_sequence", [&] { return ssd::launch_empty_sequence(p, stream); });
-    } else if (run.try_step("one_chunk", [&] { return ssd::launch_one_chunk(p, e, stream); })) {
-        // short call: the whole forward in one kernel
+    } else if (run_path == SSD_PATH_ONE_CHUNK) {
+        run.step("one_chunk", [&] { return ssd::launch_one_chunk(p, e, stream); });
+    } else if (run_path == SSD_PATH_SINGLE_PASS) {
+        run.step("chunk_scan_fused", [&] { return ssd::launch_chunk_scan_fused(p, stream); });
     } else {
-        if (e == ssd::Elem::BF16 && ssd::chunk_scan_fused_takes(p)) {
-            run.step("chunk_scan_fused", [&] { return ssd::launch_chunk_scan_fused(p, stream); });
-        } else {
         run.step("chunk_cumsum", [&] { return ssd::launch_chunk_cumsum(p, stream); });
         run.step("chunk_state", [&] {
             if (e == ssd::Elem::BF16) {
@@ -301,7 +331,6 @@ ssd_status ssd_chunk_scan_fwd_marked(const void *x, const float *dt, const float
             return ssd::launch_chunk_output(p, e, stream);
         });
         if (state_out) run.step("state_at_index", [&] { return ssd::launch_state_at_index(p, e, stream); });
-        }
     }
     if (run.err != hipSuccess)
         return fail(SSD_ERR_HIP, "%s launch failed: %s", run.failed_step, hipGetErrorString(run.err));
@@ -314,9 +343,9 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
                               float *final_state, const int32_t *state_out_idx, float *state_out,
                               const ssd_shape *shape, ssd_dtype dtype, void *workspace, size_t workspace_bytes,
                               void *hip_stream) {
-    return ssd_chunk_scan_fwd_marked(x, dt, A, B, C, D, init_state, chunk_size, y, final_state, state_out_idx,
-                                     state_out, shape, dtype, workspace, workspace_bytes, hip_stream, nullptr, 0,
-                                     nullptr, nullptr);
+    return ssd_chunk_scan_fwd_ex(x, dt, A, B, C, D, init_state, chunk_size, y, final_state, state_out_idx,
+                                 state_out, shape, dtype, workspace, workspace_bytes, hip_stream, SSD_PATH_AUTO,
+                                 nullptr, 0, nullptr, nullptr);
 }
 
 const char *ssd_status_string(ssd_status s) {

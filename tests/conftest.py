@@ -10,6 +10,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # A NaN or overflow met while converting or comparing results is a failure,
+    # not a warning.
+    config.addinivalue_line("filterwarnings", "error::RuntimeWarning")
 
 
 def pytest_collection_modifyitems(config, items):

@@ -54,41 +54,51 @@ def to_np(t):
 
 
 def gpu_run(inp, chunk=None, use_D=True, use_init=True, use_state_out=True, dev=None, return_workspace=False,
-            fill_workspace=None):
+            path=ssd.SSD_PATH_AUTO, outputs=None):
+    """One call through the C ABI.  With return_workspace the call runs the
+    chunk-parallel path (the only one with a workspace) on a zero-filled
+    workspace and the intermediates it writes are returned too.  `outputs`
+    may hold caller-allocated y / final_state / state_out tensors."""
     dev = dev or device_inputs(inp)
     chunk = chunk or inp.wl.chunk
     b, T, H, P = dev["x"].shape
     G, N = dev["B"].shape[2], dev["B"].shape[3]
     code = ssd.SSD_DTYPE_BF16 if inp.wl.dtype == "bf16" else ssd.SSD_DTYPE_F32
     shape = ssd.make_shape(b, T, H, P, N, G)
-    ws = torch.empty(max(ssd.ssd_workspace_bytes(shape, chunk, code), 1), dtype=torch.uint8, device=dev["x"].device)
-    if fill_workspace is not None:
-        ws.fill_(fill_workspace)
-    elif return_workspace:
-        ws.zero_()  # regions the path that runs leaves unwritten read as zeros, not as leftover bits
-    y, fin, sout = ssd.ssd_chunk_scan_fwd(
+    ws = None
+    if return_workspace:
+        path = ssd.SSD_PATH_CHUNK_PARALLEL
+        lay = ssd.ssd_get_workspace_layout(shape, chunk, code)
+        ws = torch.zeros(max(lay.total_bytes, 1), dtype=torch.uint8, device=dev["x"].device)
+    outputs = outputs or {}
+    y, fin, sout, names = ssd.ssd_chunk_scan_fwd_ex(
         dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"] if use_D else None,
         dev["init_state"] if use_init else None, chunk,
-        dev["state_out_idx"] if use_state_out else None, workspace=ws)
+        dev["state_out_idx"] if use_state_out else None, path=path, workspace=ws, **outputs)
     torch.cuda.synchronize()
     out = dict(y=to_np(y), final=to_np(fin), state_out=to_np(sout))
     if return_workspace:
-        cs, st, prev = ssd.workspace_views(ws, shape, chunk, code)
-        out["cs"], out["states"], out["prev"] = to_np(cs), to_np(st), to_np(prev)
+        v = ssd.workspace_views(ws, shape, chunk, code)
+        for k in ("cs", "ct", "dte", "states"):
+            out[k] = to_np(v[k])
+        # prev entry 0 is written only with an initial state.
+        first = 0 if (use_init and dev["init_state"] is not None) else 1
+        out["prev"] = to_np(v["prev"][:, first:])
     return out
 
 
-def kernel_names(inp, chunk=None, dev=None):
-    """Names of the kernels one call launches (through the marked entry point)."""
+def kernel_names(inp, chunk=None, dev=None, path=ssd.SSD_PATH_AUTO):
+    """Names of the kernels one call launches (through the timing marks of
+    ssd_chunk_scan_fwd_ex)."""
     dev = dev or device_inputs(inp)
     chunk = chunk or inp.wl.chunk
     evs = [torch.cuda.Event() for _ in range(8)]
     for e in evs:
         e.record()  # creates the event
     torch.cuda.synchronize()
-    *_, names = ssd.ssd_chunk_scan_fwd_marked(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"],
-                                              dev["init_state"], chunk, dev["state_out_idx"],
-                                              marks=[e.cuda_event for e in evs])
+    *_, names = ssd.ssd_chunk_scan_fwd_ex(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"],
+                                          dev["init_state"], chunk, dev["state_out_idx"], path=path,
+                                          marks=[e.cuda_event for e in evs])
     torch.cuda.synchronize()
     return names
 

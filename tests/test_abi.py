@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ssd.ssd_abi_version() == 5
+    assert ssd.ssd_abi_version() == 6
 
 
 def test_status_strings():
@@ -48,28 +48,57 @@ def shape(b=2, T=100, H=4, P=64, N=128, G=2):
 
 
 def test_workspace_bytes_formula():
-    s = shape()
+    s = shape()   # 8 items in bf16: the chunk-parallel path
     nc = (100 + 63) // 64
     tab = 2 * 4 * nc * 64 * 4                # cs, ct, dt_decay: fp32 [b,H,nc,Q] each
     n_st = 2 * nc * 4 * 64 * 128             # states, prev: [b,nc,H,P,N]
     n_hj = 2 * 4 * 64 * 128                  # hj: [b,H,P,N]
-    n_blk = 2 * 4 * nc * 16                  # block_decay: [b,H,nc,16]
-    n_sync = 2 + 2 * 2 * 4                   # sync: time-out word + header, two flags per (b, h)
     rnd = lambda v: (v + 255) // 256 * 256
     lay = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_BF16)
     assert lay.nchunks == nc and lay.cumsum_offset == 0
     assert lay.ct_offset == rnd(tab) and lay.dt_decay_offset == 2 * rnd(tab)
-    assert lay.block_decay_offset == 3 * rnd(tab)
-    assert lay.states_offset == 3 * rnd(tab) + rnd(4 * n_blk)
+    assert lay.states_offset == 3 * rnd(tab)
     assert lay.prev_offset == lay.states_offset + rnd(4 * n_st)
     assert lay.hj_offset == lay.prev_offset + rnd(2 * n_st)
-    assert lay.sync_offset == lay.hj_offset + rnd(4 * n_hj)
-    assert lay.total_bytes == lay.sync_offset + rnd(4 * n_sync)
+    assert lay.total_bytes == lay.hj_offset + rnd(4 * n_hj)
     assert ssd.ssd_workspace_bytes(s, 64, ssd.SSD_DTYPE_BF16) == lay.total_bytes
     lay32 = ssd.ssd_get_workspace_layout(s, 64, ssd.SSD_DTYPE_F32)
     assert lay32.hj_offset == lay32.prev_offset + rnd(4 * n_st)
-    assert lay32.total_bytes == 3 * rnd(tab) + rnd(4 * n_blk) + 2 * rnd(4 * n_st) + rnd(4 * n_hj) + rnd(4 * n_sync)
+    assert lay32.total_bytes == 3 * rnd(tab) + 2 * rnd(4 * n_st) + rnd(4 * n_hj)
     assert ssd.ssd_workspace_bytes(shape(T=0), 64, ssd.SSD_DTYPE_BF16) == 0
+    assert ssd.ssd_get_workspace_layout(shape(T=0), 64, ssd.SSD_DTYPE_BF16).total_bytes == 0
+
+
+@pytest.mark.parametrize("kw,chunk,dtype,path", [
+    (dict(), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_CHUNK_PARALLEL),            # 8 items
+    (dict(b=8, T=2048, H=80, N=128, G=1), 256, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_SINGLE_PASS),
+    (dict(b=4, T=4096, H=32, P=128, G=8), 128, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_SINGLE_PASS),
+    (dict(b=16, H=4, P=64), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_SINGLE_PASS),  # 64 items
+    (dict(b=15, H=4, P=64), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_CHUNK_PARALLEL),  # 60 items
+    (dict(b=8, T=2048, H=80, N=128, G=1), 256, ssd.SSD_DTYPE_F32, ssd.SSD_PATH_CHUNK_PARALLEL),
+    (dict(b=1, T=16384, H=64, N=256, G=1), 256, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_CHUNK_PARALLEL),
+    (dict(b=64, T=8, H=32, P=128, G=8), 128, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_ONE_CHUNK),
+    (dict(T=32), 32, ssd.SSD_DTYPE_F32, ssd.SSD_PATH_ONE_CHUNK),
+    (dict(T=33), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_CHUNK_PARALLEL),        # more than 32 tokens
+    (dict(T=20), 16, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_CHUNK_PARALLEL),        # two chunks
+    (dict(T=8, P=16, N=16), 8, ssd.SSD_DTYPE_F32, ssd.SSD_PATH_CHUNK_PARALLEL),  # headdim 16 < 1024 / 16
+    (dict(T=0), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_AUTO),
+    (dict(b=0), 64, ssd.SSD_DTYPE_BF16, ssd.SSD_PATH_AUTO),
+])
+def test_select_path(kw, chunk, dtype, path):
+    s = shape(**kw)
+    assert ssd.ssd_select_path(s, chunk, dtype) == path
+    ws = ssd.ssd_workspace_bytes(s, chunk, dtype)
+    if path == ssd.SSD_PATH_CHUNK_PARALLEL:
+        assert ws == ssd.ssd_get_workspace_layout(s, chunk, dtype).total_bytes > 0
+    else:
+        assert ws == 0
+
+
+def test_select_path_invalid():
+    with pytest.raises(ssd.SsdError):
+        ssd.ssd_select_path(shape(), 48, ssd.SSD_DTYPE_BF16)
+    assert "chunk_size" in ssd.ssd_last_error()
 
 
 @pytest.mark.parametrize("kw,chunk,code", [
@@ -114,12 +143,34 @@ class Args:
         self.p["idx"] = None
         self.p["sout"] = None
 
-    def call(self):
-        lib = ssd._load()
+    def args(self):
         v = lambda k: None if self.p[k] is None else ctypes.c_void_p(self.p[k])
-        return lib.ssd_chunk_scan_fwd(v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("init"), self.chunk,
-                                      v("y"), v("final"), v("idx"), v("sout"), ctypes.byref(self.s), self.dtype,
-                                      v("ws"), self.ws_bytes, None)
+        return (v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("init"), self.chunk, v("y"), v("final"),
+                v("idx"), v("sout"), ctypes.byref(self.s), self.dtype, v("ws"), self.ws_bytes, None)
+
+    def call(self):
+        return ssd._load().ssd_chunk_scan_fwd(*self.args())
+
+    def call_ex(self, path):
+        return ssd._load().ssd_chunk_scan_fwd_ex(*self.args(), path, None, 0, None, None)
+
+
+def test_path_errors():
+    # A path that does not take the call, or an unknown one, is refused on the host.
+    a = Args(shape())                       # 8 items, 100 tokens
+    assert a.call_ex(ssd.SSD_PATH_SINGLE_PASS) == ERR_UNSUPPORTED
+    assert a.call_ex(ssd.SSD_PATH_ONE_CHUNK) == ERR_UNSUPPORTED
+    assert a.call_ex(7) == ERR_ARGS
+    assert a.call_ex(-1) == ERR_ARGS
+    f32 = Args(shape(b=8, T=64, H=16), dtype=ssd.SSD_DTYPE_F32)
+    assert f32.call_ex(ssd.SSD_PATH_SINGLE_PASS) == ERR_UNSUPPORTED   # the single pass is bf16 only
+    # Forcing the chunk-parallel path on a call that would take the single
+    # pass needs that path's workspace.
+    sp = Args(shape(b=8, T=300, H=16))
+    assert ssd.ssd_select_path(sp.s, 64, ssd.SSD_DTYPE_BF16) == ssd.SSD_PATH_SINGLE_PASS
+    assert sp.ws_bytes == 0
+    sp.p["ws"] = None
+    assert sp.call_ex(ssd.SSD_PATH_CHUNK_PARALLEL) == ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("key", ["x", "dt", "A", "B", "C", "y"])
@@ -174,3 +225,88 @@ def test_empty_sequence_without_state_outputs_is_noop():
     a.ws_bytes = 0
     a.p["ws"] = None
     assert a.call() == OK
+
+
+# ------------------------------------------------ binding argument validation
+# CPU tensors: every check below raises before the library is asked to run.
+def _cpu_inputs(b=2, T=40, H=4, P=32, N=64, G=2, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    return dict(x=torch.zeros(b, T, H, P, dtype=dtype), dt=torch.zeros(b, T, H), A=torch.zeros(H),
+                B=torch.zeros(b, T, G, N, dtype=dtype), C=torch.zeros(b, T, G, N, dtype=dtype), D=torch.zeros(H),
+                init_state=torch.zeros(b, H, P, N), state_out_idx=torch.zeros(b, dtype=torch.int32))
+
+
+def _call(kw, **extra):
+    return ssd.ssd_chunk_scan_fwd(kw["x"], kw["dt"], kw["A"], kw["B"], kw["C"], kw["D"], kw["init_state"], 32,
+                                  kw["state_out_idx"], **extra)
+
+
+@pytest.mark.parametrize("key,bad_shape", [
+    ("C", (2, 40, 2, 32)), ("C", (2, 39, 2, 64)), ("B", (2, 39, 2, 64)), ("B", (3, 40, 2, 64)), ("dt", (2, 40, 3)), ("dt", (2, 41, 4)),
+    ("A", (5,)), ("D", (3,)), ("init_state", (2, 4, 32, 32)), ("init_state", (1, 4, 32, 64)),
+    ("state_out_idx", (3,)),
+])
+def test_binding_rejects_mis_sized_inputs(key, bad_shape):
+    import torch
+    kw = _cpu_inputs()
+    kw[key] = torch.zeros(bad_shape, dtype=kw[key].dtype)
+    with pytest.raises(ValueError, match=key):
+        _call(kw)
+
+
+@pytest.mark.parametrize("key,shape_", [("y", (2, 40, 4, 16)), ("final_state", (2, 4, 32, 32)),
+                                         ("state_out", (2, 4, 64, 32))])
+def test_binding_rejects_mis_sized_outputs(key, shape_):
+    import torch
+    kw = _cpu_inputs()
+    dtype = torch.bfloat16 if key == "y" else torch.float32
+    with pytest.raises(ValueError, match=key):
+        _call(kw, **{key: torch.zeros(shape_, dtype=dtype)})
+
+
+@pytest.mark.parametrize("key,dtype", [("dt", "float64"), ("A", "bfloat16"), ("C", "float32"),
+                                        ("state_out_idx", "int64"), ("init_state", "bfloat16")])
+def test_binding_rejects_wrong_dtypes(key, dtype):
+    import torch
+    kw = _cpu_inputs()
+    kw[key] = kw[key].to(getattr(torch, dtype))
+    with pytest.raises(TypeError, match=key):
+        _call(kw)
+
+
+def test_binding_rejects_bad_outputs_and_workspace():
+    import torch
+    kw = _cpu_inputs()
+    with pytest.raises(TypeError, match="y"):
+        _call(kw, y=torch.zeros(2, 40, 4, 32))                      # fp32 y for bf16 x
+    with pytest.raises(TypeError, match="final_state"):
+        _call(kw, final_state=torch.zeros(2, 4, 32, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        _call(kw, final_state=torch.zeros(2, 4, 64, 32).transpose(2, 3))
+    with pytest.raises(TypeError, match="workspace"):
+        _call(kw, workspace=torch.zeros(1024, dtype=torch.float32))
+    with pytest.raises(ValueError, match="workspace"):
+        _call(kw, workspace=torch.zeros(4, 256, dtype=torch.uint8))
+    no_idx = dict(kw, state_out_idx=None)
+    with pytest.raises(ValueError, match="state_out"):
+        _call(no_idx, state_out=torch.zeros(2, 4, 32, 64))
+
+
+def test_binding_rejects_non_contiguous_and_cpu():
+    kw = _cpu_inputs()
+    kw2 = dict(kw, x=kw["x"].transpose(2, 3).contiguous().transpose(2, 3))
+    with pytest.raises(ValueError, match="x must be contiguous"):
+        _call(kw2)
+    # Well-formed CPU tensors: refused, never handed to the library.
+    with pytest.raises(ValueError, match="GPU"):
+        _call(kw)
+
+
+def test_binding_rejects_bad_x():
+    import torch
+    kw = _cpu_inputs()
+    with pytest.raises(TypeError, match="x must be bfloat16 or float32"):
+        _call(dict(kw, x=kw["x"].half()))
+    with pytest.raises(ValueError):
+        _call(dict(kw, x=kw["x"][0]))

@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 5
+    assert ssd.ssd_abi_version() == 6
 
 
 # ----------------------------------------------------------- full workloads
@@ -61,19 +61,44 @@ STEP_CASES = [
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
 def test_step_chunk_cumsum(wl):
+    # The chunk-local log-decay and the two tables derived from it, element by
+    # element against their definitions on the oracle's fp64 sums.
     announce(f"chunk cumsum {wl}")
     inp = ssd_inputs.generate(wl)
     got = gpu_run(inp, return_workspace=True)
-    ref = oracle.chunk_cumsum(inp.dt, inp.A, wl.chunk)
+    ref = oracle.chunk_cumsum(inp.dt, inp.A, wl.chunk)              # [b,H,nc,Q]
     err = np.max(np.abs(got["cs"] - ref) / np.maximum(np.abs(ref), 1.0))
     print(f"  cs: max err {err:.3e}")
     assert err <= 2e-6
+    b, H, nc, Q = ref.shape
+    T = wl.seqlen
+    dt = np.zeros((b, nc * Q, H))
+    dt[:, :T] = inp.dt
+    dt = dt.reshape(b, nc, Q, H).transpose(0, 3, 1, 2)             # [b,H,nc,Q]
+    t = np.arange(nc * Q).reshape(nc, Q)
+    valid = t < T
+    # ct = cs log2(e) - log2(dt), +inf past the sequence.
+    with np.errstate(divide="ignore"):
+        ct_ref = np.where(valid, ref * np.log2(np.e) - np.log2(dt), np.inf)
+    assert np.array_equal(np.isinf(got["ct"]), np.isinf(ct_ref)), "ct: +inf entries differ"
+    fin = np.isfinite(ct_ref)
+    err = np.max(np.abs(got["ct"][fin] - ct_ref[fin]) / np.maximum(np.abs(ct_ref[fin]), 1.0))
+    print(f"  ct: max err {err:.3e}")
+    assert err <= 4e-6
+    # dte = dt_i exp(cs_e - cs_i), e = last token within the sequence of i's 32-token block.
+    e = np.minimum((t // 32) * 32 + 31, T - 1)
+    cs_e = np.take_along_axis(ref.reshape(b, H, nc * Q), e.reshape(1, 1, -1), axis=2).reshape(ref.shape)
+    dte_ref = np.where(valid, dt * np.exp(cs_e - ref), 0.0)
+    err = np.max(np.abs(got["dte"] - dte_ref) / np.maximum(np.abs(dte_ref), 1e-30))
+    print(f"  dte: max rel err {err:.3e}")
+    assert err <= 2e-5
 
 
 @pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
 def test_step_chunk_states_and_passing(wl):
-    # After the call the workspace holds each chunk's state from a zero start
-    # (green) and the state entering each chunk (yellow, the scan over chunks).
+    # After a chunk-parallel call the workspace holds each chunk's state from
+    # a zero start (green) and the state entering each chunk (yellow, the scan
+    # over chunks).
     announce(f"chunk states {wl}")
     inp = ssd_inputs.generate(wl)
     got = gpu_run(inp, return_workspace=True)
@@ -84,10 +109,9 @@ def test_step_chunk_states_and_passing(wl):
         sl = slice(t0, min(t0 + Q, T))
         _, fin, _, _ = oracle.ssd_forward(inp.x[:, sl], inp.dt[:, sl], inp.A, inp.B[:, sl], inp.C[:, sl])
         zero_start.append(fin)
-    if "state_pass" in kernel_names(inp):
-        check("chunk states from a zero start", got["states"], np.stack(zero_start, axis=1), TOL[wl.dtype])
+    check("chunk states from a zero start", got["states"], np.stack(zero_start, axis=1), TOL[wl.dtype])
     first = 0 if wl.init_state else 1  # entry 0 is written only with an initial state
-    check("states entering each chunk", got["prev"][:, first:], ref["chunk_states"][:, first:], TOL[wl.dtype])
+    check("states entering each chunk", got["prev"], ref["chunk_states"][:, first:], TOL[wl.dtype])
     check("final_state", got["final"], ref["final"], TOL[wl.dtype])
 
 
@@ -180,41 +204,57 @@ def test_two_halves(m):
     check("halves y vs one call", y, full["y"], 2e-2)
 
 
-def test_determinism():
-    wl = ssd_inputs.WORKLOADS["llama3_8b_hybrid"]
-    wl = workload("determinism", 2, 1000, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk, "bf16",
-                  init_state=True, state_out=True, seed=71)
-    announce(f"determinism {wl}")
+# One case per path: chunk-parallel (32 items), single pass (128 items, split
+# into block ranges) and one_chunk (8 tokens).
+PATH_CASES = [
+    ("chunk_parallel", (2, 1000, 8, 128, 128, 2, 128), ssd.SSD_PATH_CHUNK_PARALLEL),
+    ("single_pass", (2, 1000, 64, 64, 128, 1, 256), ssd.SSD_PATH_SINGLE_PASS),
+    ("one_chunk", (8, 8, 32, 128, 128, 8, 64), ssd.SSD_PATH_ONE_CHUNK),
+]
+
+
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_determinism(case):
+    name, (b, T, H, P, N, G, Q), path = case
+    wl = workload("determinism_" + name, b, T, H, P, N, G, Q, "bf16", init_state=True, state_out=True, seed=71)
+    announce(f"determinism {wl} path={name}")
     inp = ssd_inputs.generate(wl)
     dev = device_inputs(inp)
+    assert ssd.ssd_select_path(ssd.make_shape(b, T, H, P, N, G), Q, ssd.SSD_DTYPE_BF16) == path
     runs = [gpu_run(inp, dev=dev) for _ in range(3)]
     for r in runs[1:]:
         for k in ("y", "final", "state_out"):
             assert np.array_equal(r[k], runs[0][k]), f"{k} differs between identical calls"
+    ref = oracle_run(inp)
+    check("y", runs[0]["y"], ref["y"], TOL["bf16"])
 
 
-def test_guard_canaries():
-    wl = workload("canaries", 2, 200, 4, 64, 128, 2, 64, "bf16", init_state=True, state_out=True, seed=81)
-    announce(f"canaries {wl}")
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_guard_canaries(case):
+    # Outputs inside NaN-filled guard regions: nothing is written outside them
+    # and every element inside is written.
+    name, (b, T, H, P, N, G, Q), path = case
+    wl = workload("canaries_" + name, b, T, H, P, N, G, Q, "bf16", init_state=True, state_out=True, seed=81)
+    announce(f"canaries {wl} path={name}")
     inp = ssd_inputs.generate(wl)
     dev = device_inputs(inp)
     pad = 4096
+
     def guarded(n, dtype):
         buf = torch.full((n + 2 * pad,), float("nan"), dtype=dtype, device="cuda")
         return buf, buf[pad:pad + n]
+
     ybuf, y = guarded(dev["x"].numel(), torch.bfloat16)
-    n_state = 2 * 4 * 64 * 128
-    fbuf, fin = guarded(n_state, torch.float32)
-    sbuf, sout = guarded(n_state, torch.float32)
-    ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], dev["init_state"], 64,
-                           dev["state_out_idx"], y=y.view(dev["x"].shape), final_state=fin.view(2, 4, 64, 128),
-                           state_out=sout.view(2, 4, 64, 128))
-    torch.cuda.synchronize()
+    fbuf, fin = guarded(b * H * P * N, torch.float32)
+    sbuf, sout = guarded(b * H * P * N, torch.float32)
+    outs = dict(y=y.view(dev["x"].shape), final_state=fin.view(b, H, P, N), state_out=sout.view(b, H, P, N))
+    got = gpu_run(inp, dev=dev, path=path, outputs=outs)
     for buf in (ybuf, fbuf, sbuf):
         assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[-pad:].float()).all(), "write outside output"
         assert torch.isfinite(buf[pad:-pad].float()).all(), "output not fully written"
     ref = oracle_run(inp)
-    check("y", y.view(dev["x"].shape).float().cpu().numpy(), ref["y"], 2e-2)
+    for k in ("y", "final", "state_out"):
+        check(k, got[k], ref[k], TOL["bf16"])
 
 
 # ---------------------------------------------------------------- edge cases
@@ -348,10 +388,43 @@ def test_fused_forward(case):
     check("final_state", got["final"], ref["final"], TOL["bf16"])
     if sout:
         check("state_out", got["state_out"], ref["state_out"], TOL["bf16"])
-    # Run again on a workspace filled with nonzero bytes (the single pass
-    # must not depend on its contents): the same bits.
-    again = gpu_run(inp, dev=dev, use_D=use_D, fill_workspace=0xFF)
-    assert np.array_equal(again["y"], got["y"]) and np.array_equal(again["final"], got["final"])
+
+
+# Degenerate values through the single pass: dt = 0 tokens (no input, no
+# decay; ct = +inf) at the start, inside a block, across a block boundary and
+# at the end, and A = 0 heads (no decay at all: the state is a plain sum).
+@pytest.mark.parametrize("zero_dt,zero_A", [(True, False), (False, True), (True, True)])
+def test_fused_degenerate_values(zero_dt, zero_A):
+    b, T, H, P, N, G, Q = 2, 700, 64, 64, 128, 2, 256
+    wl = workload("fused_degenerate", b, T, H, P, N, G, Q, "bf16", init_state=True, state_out=True, seed=241)
+    announce(f"fused degenerate {wl} dt=0 tokens: {zero_dt} A=0 heads: {zero_A}")
+    inp = ssd_inputs.generate(wl)
+    if zero_dt:
+        for t in (0, 1, 50, 127, 128, 129, 300, 301, 302, T - 1):
+            inp.dt[:, t, :] = 0.0
+        inp.dt[1, 400:460, 5] = 0.0
+    if zero_A:
+        inp.A[::3] = 0.0
+    inp.state_out_idx = np.array([0, 129], np.int32)
+    dev = device_inputs(inp)
+    assert kernel_names(inp, dev=dev) == ["chunk_scan_fused"]
+    got, ref = gpu_run(inp, dev=dev), oracle_run(inp)
+    for k in ("y", "final", "state_out"):
+        check(k, got[k], ref[k], TOL["bf16"])
+
+
+def test_paths_agree_at_layer_shape():
+    # The 2.7B layer's shape (fewer tokens) through the single pass and the
+    # chunk-parallel kernels, each against the oracle.
+    wl = workload("paths", 2, 1100, 80, 64, 128, 1, 256, "bf16", init_state=True, state_out=True, seed=251)
+    announce(f"both paths {wl}")
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp)
+    ref = oracle_run(inp)
+    for path in (ssd.SSD_PATH_SINGLE_PASS, ssd.SSD_PATH_CHUNK_PARALLEL):
+        got = gpu_run(inp, dev=dev, path=path)
+        for k in ("y", "final", "state_out"):
+            check(f"{ssd.PATH_NAMES[path]} {k}", got[k], ref[k], TOL["bf16"])
 
 
 def test_fused_in_place():
