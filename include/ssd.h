@@ -233,6 +233,34 @@ ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
                                  int path, void *const *marks, int n_marks, int *n_kernels,
                                  const char **kernel_names);
 
+/* Bytes of the library's static device scratch (64 MiB), the workspace of
+ * ssd_chunk_scan_fwd_noalloc. */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* ssd_chunk_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  A call that needs a workspace (the
+ * chunk-parallel path, ssd_workspace_bytes(...) > 0) uses a static array of
+ * SSD_NOALLOC_SCRATCH_BYTES in the library's device code instead; every GPU
+ * holds its own copy until the process ends, and its device address is
+ * looked up once per GPU on the first such call there.  Neither this entry
+ * point nor anything it calls allocates or frees memory.
+ *   - Calls needing more than SSD_NOALLOC_SCRATCH_BYTES return
+ *     SSD_ERR_WORKSPACE before anything is enqueued.
+ *   - hip_stream must belong to the current device (else SSD_ERR_ARGS).
+ *   - All calls on one GPU share its scratch: calls that may overlap in time
+ *     on one GPU (on different streams, or from several threads without
+ *     ordering) race and give unspecified results.  Calls in one stream's
+ *     order are safe.  The scratch keeps the last call's intermediates;
+ *     nothing in a call depends on what it held before.
+ * Arguments, results and every other error are as for ssd_chunk_scan_fwd. */
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const float *init_state, int chunk_size,
+                                      void *y, float *final_state,
+                                      const int32_t *state_out_idx, float *state_out,
+                                      const ssd_shape *shape, ssd_dtype dtype, void *hip_stream);
+
 /* Static description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "SsdError", "ssd_abi_version", "ssd_status_string", "ssd_last_error", "ssd_workspace_bytes",
     "ssd_get_workspace_layout", "ssd_select_path", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_ex",
-    "workspace_views", "library_path", "SSD_PATH_AUTO", "SSD_PATH_ONE_CHUNK", "SSD_PATH_SINGLE_PASS",
+    "ssd_chunk_scan_fwd_noalloc", "SSD_NOALLOC_SCRATCH_BYTES", "workspace_views", "library_path", "SSD_PATH_AUTO", "SSD_PATH_ONE_CHUNK", "SSD_PATH_SINGLE_PASS",
     "SSD_PATH_CHUNK_PARALLEL",
 ]
 
@@ -26,6 +26,7 @@ _lib = None
 
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_BF16 = 1
+SSD_NOALLOC_SCRATCH_BYTES = 64 << 20
 SSD_PATH_AUTO = 0
 SSD_PATH_ONE_CHUNK = 1
 SSD_PATH_SINGLE_PASS = 2
@@ -85,6 +86,8 @@ def _load():
                                           i32, ctypes.POINTER(vp), i32, ctypes.POINTER(i32),
                                           ctypes.POINTER(ctypes.c_char_p)]
     lib.ssd_chunk_scan_fwd_ex.restype = i32
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -174,6 +177,20 @@ def ssd_chunk_scan_fwd_ex(x, dt, A, B, C, D=None, init_state=None, chunk_size: i
                 state_out, workspace, stream, int(path), list(marks))
 
 
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, init_state=None, chunk_size: int = 256,
+                               state_out_idx=None, *, y=None, final_state=None, return_final_state: bool = True,
+                               state_out=None, stream=None):
+    """ssd_chunk_scan_fwd through the entry point that allocates nothing: a
+    workspace, when the call needs one, is the library's static device
+    scratch (at most SSD_NOALLOC_SCRATCH_BYTES).  Pass y, final_state and
+    state_out to allocate nothing here either; missing ones are allocated
+    by torch before the call."""
+    y, final_state, state_out, _ = _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state,
+                                        return_final_state, state_out, None, stream, SSD_PATH_AUTO, None,
+                                        noalloc=True)
+    return y, final_state, state_out
+
+
 def _expect(name, t, shape, dtype, device):
     """Checks one tensor argument; `shape` is the exact shape required."""
     if tuple(t.shape) != tuple(shape):
@@ -187,7 +204,7 @@ def _expect(name, t, shape, dtype, device):
 
 
 def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state, return_final_state, state_out,
-         workspace, stream, path, marks):
+         workspace, stream, path, marks, noalloc=False):
     import torch
 
     if x.dim() != 4 or B.dim() != 4:
@@ -235,10 +252,16 @@ def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_stat
         final_state = torch.empty(state_shape, dtype=torch.float32, device=dev)
     if state_out_idx is not None and state_out is None:
         state_out = torch.empty(state_shape, dtype=torch.float32, device=dev)
-    if workspace is None and ws_bytes > 0:
+    if workspace is None and ws_bytes > 0 and not noalloc:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    if noalloc:
+        _check(lib.ssd_chunk_scan_fwd_noalloc(
+            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), int(chunk_size), _ptr(y),
+            _ptr(final_state), _ptr(state_out_idx), _ptr(state_out), ctypes.byref(shape), code,
+            ctypes.c_void_p(stream) if stream else None))
+        return y, final_state, state_out, None
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), int(chunk_size), _ptr(y),
             _ptr(final_state), _ptr(state_out_idx), _ptr(state_out), ctypes.byref(shape), code, _ptr(workspace),
             int(workspace.numel()) if workspace is not None else 0, ctypes.c_void_p(stream) if stream else None)

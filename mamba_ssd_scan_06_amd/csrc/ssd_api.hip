@@ -21,6 +21,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "ssd.h"
@@ -175,6 +176,47 @@ struct Launcher {
         record(name, launch());
     }
 };
+
+}  // namespace
+
+// Workspace of ssd_chunk_scan_fwd_noalloc: every GPU the library runs on holds
+// its own copy from the time the library's device code is loaded there until
+// the process ends.  In host code `scratch` only names the variable; its
+// device address on each GPU comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, looked up once
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with it current).  `stream` must belong to it.
+ssd_status scratch_ptr(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SSD_ERR_HIP, "device %d beyond the %d supported", dev, kMaxDevices);
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return fail(SSD_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(SSD_ERR_ARGS, "hip_stream belongs to device %d, the current device is %d", (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(SSD_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
 
 }  // namespace
 
@@ -346,6 +388,25 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
     return ssd_chunk_scan_fwd_ex(x, dt, A, B, C, D, init_state, chunk_size, y, final_state, state_out_idx,
                                  state_out, shape, dtype, workspace, workspace_bytes, hip_stream, SSD_PATH_AUTO,
                                  nullptr, 0, nullptr, nullptr);
+}
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                                      const float *D, const float *init_state, int chunk_size, void *y,
+                                      float *final_state, const int32_t *state_out_idx, float *state_out,
+                                      const ssd_shape *shape, ssd_dtype dtype, void *hip_stream) {
+    ssd_status st = check_shape(shape, chunk_size, dtype);
+    if (st != SSD_OK) return st;
+    const size_t need = ssd_workspace_bytes(shape, chunk_size, dtype);
+    if (need > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+        return fail(SSD_ERR_WORKSPACE, "the call needs %zu bytes of workspace, the static scratch holds %zu", need,
+                    (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_ptr(static_cast<hipStream_t>(hip_stream), &ws);
+        if (st != SSD_OK) return st;
+    }
+    return ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, chunk_size, y, final_state, state_out_idx, state_out,
+                              shape, dtype, ws, need > 0 ? (size_t)SSD_NOALLOC_SCRATCH_BYTES : 0, hip_stream);
 }
 
 const char *ssd_status_string(ssd_status s) {
