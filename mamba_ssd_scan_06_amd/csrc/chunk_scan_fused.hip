@@ -108,10 +108,10 @@ struct FusedCfg {
     static constexpr int NTW = NT / WPN, PTW = PT / WPP;
     static constexpr int UXR = Q * WX / THREADS;        // 16-byte x pieces per thread
     static constexpr int UBR = Q * WB / THREADS;        // 16-byte B pieces per thread
-    // Per-block tables in LDS (floats): cs2, ct, dte per token, then cs2 at
-    // the end of each 32-token block and the Horner factors.
-    static constexpr int TB_CS2 = 0, TB_CT = Q, TB_DTE = 2 * Q, TB_CE = 3 * Q, TB_G = 3 * Q + NBLK;
-    static constexpr int TB_SIZE = 3 * Q + 2 * NBLK;
+    // Per-block tables in LDS (floats): cs2, ct, dte and wl per token, then
+    // cs2 at the end of each 32-token block.
+    static constexpr int TB_CS2 = 0, TB_CT = Q, TB_DTE = 2 * Q, TB_WL = 3 * Q, TB_CE = 4 * Q;
+    static constexpr int TB_SIZE = 4 * Q + NBLK;
     // LDS rows are padded by 32 bytes, so that every fragment address is one
     // per-lane base plus an immediate offset, and consecutive rows start on
     // different banks.  (A 16-byte pad measured twice the bank conflicts.)
@@ -155,7 +155,7 @@ void chunk_scan_fused_kernel(Params p) {
     constexpr int N = Cf::N, P = Cf::P, Q = Cf::Q, KS = Cf::KS, WB = Cf::WB, WX = Cf::WX;
     constexpr int W = Cf::W, THREADS = Cf::THREADS, NBLK = Cf::NBLK, TPL = Cf::TPL;
     static_assert(THREADS == 4 * QB, "launch bounds");
-    constexpr int TB_CS2 = Cf::TB_CS2, TB_CT = Cf::TB_CT, TB_DTE = Cf::TB_DTE, TB_CE = Cf::TB_CE, TB_G = Cf::TB_G;
+    constexpr int TB_CS2 = Cf::TB_CS2, TB_CT = Cf::TB_CT, TB_DTE = Cf::TB_DTE, TB_WL = Cf::TB_WL, TB_CE = Cf::TB_CE;
     constexpr int NTW = Cf::NTW, PTW = Cf::PTW, UXR = Cf::UXR, UBR = Cf::UBR;
     constexpr int SB = Cf::SB, SX = Cf::SX, SH = Cf::SH;
     constexpr int RX = THREADS / WX, RB = THREADS / WB;  // rows between a thread's x / B pieces
@@ -383,29 +383,27 @@ void chunk_scan_fused_kernel(Params p) {
         double sl = se[0];
 #pragma unroll
         for (int m = 1; m < NBLK; ++m) sl = mb == m ? se[m] : sl;
+        // se[NBLK - 1] is the sum at the block's last token Qc - 1.
         typedef float FV __attribute__((ext_vector_type(TPL)));
-        FV c, ct, de;
+        FV c, ct, de, wv;
 #pragma unroll
         for (int v = 0; v < TPL; ++v) {
             const bool in = i0 + v < Qc;
             c[v] = (float)(a * sv[v] * kLog2eD);
             ct[v] = in ? c[v] - log2f(dtr[v]) : __builtin_inff();
             de[v] = in ? dtr[v] * exp_neg((float)(a * (sl - sv[v]))) : 0.f;
+            wv[v] = in ? dtr[v] * exp_neg((float)(a * (se[NBLK - 1] - sv[v]))) : 0.f;
         }
         *reinterpret_cast<FV *>(tb + TB_CS2 + i0) = c;
         *reinterpret_cast<FV *>(tb + TB_CT + i0) = ct;
         *reinterpret_cast<FV *>(tb + TB_DTE + i0) = de;
-        // Per 32-token block m (lane m < NBLK): cs2 at e(m) and the Horner
-        // factor exp(cs_e(m) - cs_e(m-1)) (exp(cs_e(0)) for m = 0).
+        *reinterpret_cast<FV *>(tb + TB_WL + i0) = wv;
+        // cs2 at the end e(m) of each 32-token block m (lane m < NBLK).
         if (ln < NBLK) {
-            double sm = se[0], sp = 0.0;
+            double sm = se[0];
 #pragma unroll
-            for (int m = 1; m < NBLK; ++m) {
-                sm = ln == m ? se[m] : sm;
-                sp = ln == m ? se[m - 1] : sp;
-            }
+            for (int m = 1; m < NBLK; ++m) sm = ln == m ? se[m] : sm;
             tb[TB_CE + ln] = (float)(a * sm * kLog2eD);
-            tb[TB_G + ln] = exp_neg((float)(a * (sm - sp)));
         }
     };
 
@@ -504,7 +502,6 @@ void chunk_scan_fused_kernel(Params p) {
 
     // ---- per-block factors (uniform).
     float ce[NBLK];   // cs2 at the end of each 32-token block
-    float gst[NBLK];  // state Horner factors
     int Qc = 0, nblk = 0;
     bool live = false, full = false;
 
@@ -532,86 +529,74 @@ void chunk_scan_fused_kernel(Params p) {
                 }
         }
 #pragma unroll
-        for (int m = 0; m < NBLK; ++m) {
+        for (int m = 0; m < NBLK; ++m)
             ce[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[TB_CE + m])));
-            gst[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tb[TB_G + m])));
-        }
     };
 
-    // Blue, orange and the D skip of a full step, for the wave's rows.
-    auto outputs = [&](const Step &st, const float *tb, f32x4 (&acc)[PT]) __attribute__((always_inline)) {
-        const float dh = dh_of(st);
-        const bool has_prev = st.c > 0 || p.init_state != nullptr;
-        const float cs2i = tb[TB_CS2 + 16 * tile + il];
-        // Blue: exp(cs_i) C_i . h_{c-1} (rows p, column i).
-        if (has_prev) {
+    // Blue for the wave's rows: exp(cs_i) C_i . h_{c-1} (rows p, column i).
+    auto blue = [&](const float cs2i, f32x4 (&acc)[PT]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int q = 0; q < PT; ++q)
+        for (int q = 0; q < PT; ++q)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) mma(lds16(hb + hR + 16 * q * SH + 64 * ks), cf[ks], acc[q]);
-            const float ei = exp2_hw(cs2i);
+            for (int ks = 0; ks < KS; ++ks) mma(lds16(hb + hR + 16 * q * SH + 64 * ks), cf[ks], acc[q]);
+        const float ei = exp2_hw(cs2i);
 #pragma unroll
-            for (int q = 0; q < PT; ++q) acc[q] = acc[q] * ei;
+        for (int q = 0; q < PT; ++q) acc[q] = acc[q] * ei;
+    };
+    // G^T of 32-token block m, half `half`, for the wave's rows: lane (il,
+    // grp) holds G^T[j][i], i = 16 tile + il, j = 32m + 16half + 4grp + r.
+    auto g_half = [&](int m, int half) __attribute__((always_inline)) {
+        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma(lds16(bl + bR + (kStep * m + 16 * half) * SB + 64 * ks), cf[ks], a4);
+        return a4;
+    };
+    // Orange factors of block m below the diagonal block md: G times
+    // exp2(cs2_i - cs2_e(m)) dte_j, rounded to bf16 once (applied to raw x).
+    auto orange_below = [&](int m, const float *tb, float cs2i) __attribute__((always_inline)) {
+        const float ai = exp2_hw(cs2i - ce[m]);
+        f32x4 w0, w1;
+        slot_pair(tb + TB_DTE, m, w0, w1);
+        Frag<T> gf;
+        const f32x4 g0 = g_half(m, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gf.set(r, g0[r] * (ai * w0[r]));
+        const f32x4 g1 = g_half(m, 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gf.set(4 + r, g1[r] * (ai * w1[r]));
+        return gf;
+    };
+    // Orange factors of the diagonal block md: G times the exact factors
+    // exp2(cs2_i - ct_j) (the exponent is at most log2(dt_j) for j <= i;
+    // above the diagonal the product is replaced by 0), plus D at j = i (the
+    // skip term), rounded to bf16 once (applied to raw x).  j - i = 16 half +
+    // r - di, with di from an opaque copy so that the comparisons are made
+    // here and not kept across the loop.
+    auto orange_diag = [&](const float *tb, float cs2i, float dh) __attribute__((always_inline)) {
+        int di = 16 * (tile & 1) + il - 4 * grp;
+        asm volatile("" : "+v"(di));
+        f32x4 ct0, ct1;
+        slot_pair(tb + TB_CT, md, ct0, ct1);
+        Frag<T> lf;
+        const f32x4 g0 = g_half(md, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // above the diagonal the factor may overflow; the select drops it
+            const float v = r > di ? 0.f : g0[r] * exp2_hw(cs2i - ct0[r]);
+            lf.set(r, r == di ? v + dh : v);
         }
-        // G^T of block m, half `half`, for the wave's rows: lane (il, grp)
-        // holds G^T[j][i], i = 16 tile + il, j = 32m + 16half + 4grp + r.
-        auto g_half = [&](int m, int half) __attribute__((always_inline)) {
-            f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mma(lds16(bl + bR + (kStep * m + 16 * half) * SB + 64 * ks), cf[ks], a4);
-            return a4;
-        };
-        // Orange below the diagonal block: G times exp2(cs2_i - cs2_e(m)) dte_j,
-        // rounded to bf16 once, on raw x.
-        static_for<NBLK - 1>([&](auto mc) __attribute__((always_inline)) {
-            constexpr int m = decltype(mc)::value;
-            if (m >= md) return;
-            const float ai = exp2_hw(cs2i - ce[m]);
-            f32x4 w0, w1;
-            slot_pair(tb + TB_DTE, m, w0, w1);
-            Frag<T> gf;
-            const f32x4 g0 = g_half(m, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gf.set(r, g0[r] * (ai * w0[r]));
-            const f32x4 g1 = g_half(m, 1);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gf.set(4 + r, g1[r] * (ai * w1[r]));
-#pragma unroll
-            for (int q = 0; q < PT; ++q) mma(read_tr(xs + xT + kStep * m * SX + 32 * q, 16 * SX), gf, acc[q]);
-        });
-        // Diagonal block md: G times the exact factors exp2(cs2_i - ct_j)
-        // (the exponent is at most log2(dt_j) for j <= i; above the diagonal
-        // the product is replaced by 0), plus D at j = i (the skip term),
-        // rounded to bf16 once, on raw x.  j - i = 16 half + r - di, with di
-        // from an opaque copy so that the comparisons are made here and not
-        // kept across the loop.
-        {
-            int di = 16 * (tile & 1) + il - 4 * grp;
-            asm volatile("" : "+v"(di));
-            f32x4 ct0, ct1;
-            slot_pair(tb + TB_CT, md, ct0, ct1);
-            Frag<T> lf;
-            const f32x4 g0 = g_half(md, 0);
+        if (tile & 1) {
+            const f32x4 g1 = g_half(md, 1);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // above the diagonal the factor may overflow; the select drops it
-                const float v = r > di ? 0.f : g0[r] * exp2_hw(cs2i - ct0[r]);
-                lf.set(r, r == di ? v + dh : v);
+                const float v = 16 + r > di ? 0.f : g1[r] * exp2_hw(cs2i - ct1[r]);
+                lf.set(4 + r, 16 + r == di ? v + dh : v);
             }
-            if (tile & 1) {
-                const f32x4 g1 = g_half(md, 1);
+        } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = 16 + r > di ? 0.f : g1[r] * exp2_hw(cs2i - ct1[r]);
-                    lf.set(4 + r, 16 + r == di ? v + dh : v);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lf.set(4 + r, 0.f);  // rows above the diagonal
-            }
-#pragma unroll
-            for (int q = 0; q < PT; ++q) mma(read_tr(xs + xT + kStep * md * SX + 32 * q, 16 * SX), lf, acc[q]);
+            for (int r = 0; r < 4; ++r) lf.set(4 + r, 0.f);  // rows above the diagonal
         }
+        return lf;
     };
     // y, rounded; rows past the sequence fall outside the buffer (and with
     // on = false every store is dropped).  y is written once and not read
@@ -647,81 +632,108 @@ void chunk_scan_fused_kernel(Params p) {
         }
     };
 
-    // One step (tables in tb): the outputs if the step is full, (wave 0) the
-    // next step's tables, then the state (and the state after the accepted
-    // index if it lies in the step).  The next step's C rows are fetched
-    // before the state part, which covers their latency.
-    auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
-        __attribute__((always_inline)) {
-        {
-            f32x4 acc[PT];
+    // The state after an accepted index j in this step (position jl, 32-token
+    // block mj), from the state entering the step (hs, before the step's
+    // update): h_j = exp(cs_j) h_{c-1} + sum over tokens s <= j of B_s^T x_s
+    // with the exact factors exp2(cs2_j - ct_s), stored to state_out.  Runs
+    // at most once per item.
+    auto state_at_index = [&](const Step &st, const float *tb, int jl) __attribute__((always_inline)) {
+        const int mj = jl / kStep;
+        const float ej = exp2_hw(tb[TB_CS2 + jl]);
+        f32x4 hv[NTW][PTW];
 #pragma unroll
-            for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (live) outputs(st, tb, acc);
-            store_y(st, live, acc);
-        }
-        if (has_next && wave == 0) make_tables(nx, tb_next);
-        load_c(nx, has_next && nx.c >= nx.c0);
-        // Accepted index j in this step: its 32-token block mj and its
-        // position jl in the step (uniform; -1 if not here).
-        int jl = -1;
-        if (full) {
-            const int64_t j = j_of(st);
-            if (j >= 0 && j / Q == st.c) jl = (int)(j - (int64_t)st.c * Q);
-        }
-        const int mj = jl >= 0 ? jl / kStep : -1;
-        // State: h_c = exp(cs_last) h_{c-1} + B^T (w x), Horner over the
-        // 32-token blocks.  In the block mj holding j, first the state after
-        // j: the state at the end of the previous 32-token block times
-        // exp(cs_j - cs_e(mj-1)) plus the tokens s <= j of block mj with
-        // their exact factors exp2(cs2_j - ct_s), stored to state_out.
-        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
-            constexpr int m = decltype(mc)::value;
-            if (m >= nblk) return;
-            Frag<T> fa[NTW], fb[PTW];
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) hv[a][q] = hs[a][q] * ej;
+        const float cs2j = tb[TB_CS2 + jl];
+        for (int m = 0; m <= mj; ++m) {
+            Frag<T> fa[NTW];
 #pragma unroll
             for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + bT + kStep * m * SB + 32 * a, 16 * SB);
+            int j4 = jl - 4 * grp;  // slot r of half 0 is token 32m + 4grp + r
+            asm volatile("" : "+v"(j4));
+            f32x4 c0, c1, w0, w1;
+            slot_pair(tb + TB_CT, m, c0, c1);
 #pragma unroll
-            for (int q = 0; q < PTW; ++q) fb[q] = read_tr(xs + xS + kStep * m * SX + 32 * q, 16 * SX);
-            if (m == mj) {
-                const float cs2j = tb[TB_CS2 + jl];
-                const float ej = exp2_hw(m == 0 ? cs2j : cs2j - ce[m > 0 ? m - 1 : 0]);
-                int j4 = jl - 4 * grp;  // slot r of half 0 is token 32m + 4grp + r
-                asm volatile("" : "+v"(j4));
-                f32x4 c0, c1, w0, w1;
-                slot_pair(tb + TB_CT, m, c0, c1);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    w0[r] = kStep * m + r > j4 ? 0.f : exp2_hw(cs2j - c0[r]);
-                    w1[r] = kStep * m + 16 + r > j4 ? 0.f : exp2_hw(cs2j - c1[r]);
-                }
-                uint32_t so[NTW][PTW];
-                state_offsets(so);
-                float *dst = p.state_out + (int64_t)st.item * P * N;
-#pragma unroll
-                for (int a = 0; a < NTW; ++a) {
-                    Frag<T> fw = fa[a];
-                    scale_frag(fw, w0, w1);
-#pragma unroll
-                    for (int q = 0; q < PTW; ++q) {
-                        f32x4 hv = hs[a][q] * ej;
-                        mma(fw, fb[q], hv);
-                        *reinterpret_cast<f32x4 *>(dst + so[a][q]) = hv;
-                    }
-                }
+            for (int r = 0; r < 4; ++r) {
+                w0[r] = kStep * m + r > j4 ? 0.f : exp2_hw(cs2j - c0[r]);
+                w1[r] = kStep * m + 16 + r > j4 ? 0.f : exp2_hw(cs2j - c1[r]);
             }
-            f32x4 w0, w1;
-            slot_pair(tb + TB_DTE, m, w0, w1);
 #pragma unroll
             for (int a = 0; a < NTW; ++a) scale_frag(fa[a], w0, w1);
 #pragma unroll
-            for (int a = 0; a < NTW; ++a)
+            for (int q = 0; q < PTW; ++q) {
+                const Frag<T> fb = read_tr(xs + xS + kStep * m * SX + 32 * q, 16 * SX);
 #pragma unroll
-                for (int q = 0; q < PTW; ++q) {
-                    hs[a][q] = hs[a][q] * gst[m];
-                    mma(fa[a], fb[q], hs[a][q]);
+                for (int a = 0; a < NTW; ++a) mma(fa[a], fb, hv[a][q]);
+            }
+        }
+        uint32_t so[NTW][PTW];
+        state_offsets(so);
+        float *dst = p.state_out + (int64_t)st.item * P * N;
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(dst + so[a][q]) = hv[a][q];
+    };
+
+    // One step (tables in tb).  With the outputs (a full step): blue, then
+    // one pass over the 32-token blocks m that reads each block's x
+    // fragments once for both products: the orange part of the wave's rows
+    // (m <= md) and the state update
+    //   h_c = exp(cs_last) h_{c-1} + sum_j wl_j B_j^T x_j,
+    //   wl_j = dt_j exp(cs_last - cs_j) <= dt_j  (the weighted B fragment
+    //   formed from the transposed B read and rounded once),
+    // then y.  The next step's C rows are fetched once the wave's last
+    // C . B^T product is issued, and wave 0 makes the next step's tables at
+    // the end of its work (its rows meet the fewest blocks).
+    auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
+        __attribute__((always_inline)) {
+        if (full) {
+            const int64_t j = j_of(st);
+            if (j >= 0 && j / Q == st.c) state_at_index(st, tb, (int)(j - (int64_t)st.c * Q));
+        }
+        f32x4 acc[PT];
+#pragma unroll
+        for (int q = 0; q < PT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float cs2i = tb[TB_CS2 + 16 * tile + il];
+        const float dh = dh_of(st);
+        if (live && (st.c > 0 || p.init_state != nullptr)) blue(cs2i, acc);
+        const float gl = exp2_hw(ce[NBLK - 1]);  // exp(cs_last)
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int q = 0; q < PTW; ++q) hs[a][q] = hs[a][q] * gl;
+        static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            if (m >= nblk) return;
+            const bool orange = live && m <= md;
+            Frag<T> of;
+            if (live && m < md) of = orange_below(m, tb, cs2i);
+            if (live && m == md) of = orange_diag(tb, cs2i, dh);
+            Frag<T> fa[NTW];
+#pragma unroll
+            for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + bT + kStep * m * SB + 32 * a, 16 * SB);
+            f32x4 w0, w1;
+            slot_pair(tb + TB_WL, m, w0, w1);
+#pragma unroll
+            for (int a = 0; a < NTW; ++a) scale_frag(fa[a], w0, w1);
+            // Each x fragment of the block feeds the orange product of the
+            // wave's rows and the state update of the wave's p tiles
+            // pw PTW .. pw PTW + PTW - 1.
+#pragma unroll
+            for (int q = 0; q < PT; ++q) {
+                const Frag<T> xf = read_tr(xs + xT + kStep * m * SX + 32 * q, 16 * SX);
+                if (orange) mma(xf, of, acc[q]);
+                if (Cf::WPP == 1 || q / PTW == pw) {
+#pragma unroll
+                    for (int a = 0; a < NTW; ++a) mma(fa[a], xf, hs[a][q % PTW]);
                 }
+            }
         });
+        load_c(nx, has_next && nx.c >= nx.c0);
+        store_y(st, live, acc);
+        if (has_next && wave == 0) make_tables(nx, tb_next);
     };
 
     // ---- prologue: the first step's inputs and tables.  The tables of
