@@ -463,38 +463,35 @@ void chunk_scan_fused_kernel(Params p) {
         const int j = ((const __attribute__((address_space(4))) int *)(uintptr_t)p.state_out_idx)[st.b];
         return j < 0 ? -1 : min((int64_t)j, L - 1);
     };
-    // Start a unit: h_{-1} is the initial state (or 0).  The unit holding
-    // block 0 in its range also answers an accepted index of -1 (nothing
-    // accepted: the initial state).
-    auto begin_unit = [&](const Step &st) __attribute__((always_inline)) {
+    // The item's rows of a head's state, as a buffer: item * P * N = (bh * PF
+    // + s * P) * N.  With on = false (or no tensor) it covers no bytes.
+    auto state_rows = [&](const float *base, const Step &st, bool on) {
+        return rsrc(base + (int64_t)st.item * P * N, on && base != nullptr ? (uint32_t)(P * N * 4) : 0u);
+    };
+    // State loads and stores are rare (an item's first and last steps, and
+    // the step holding its accepted index) and issued only where needed.
+    // A unit starts from h_{-1}, the initial state (or 0), loaded at the
+    // switch into it.
+    auto load_init = [&](const Step &st) __attribute__((always_inline)) {
+        const auto r = state_rows(p.init_state, st, true);
         uint32_t so[NTW][PTW];
         state_offsets(so);
-        // item * P * N = (bh * PF + s * P) * N: the item's rows of its head's state
-        const int64_t hst = (int64_t)st.item * P * N;
 #pragma unroll
         for (int a = 0; a < NTW; ++a)
 #pragma unroll
             for (int q = 0; q < PTW; ++q)
-                hs[a][q] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + hst + so[a][q])
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
-        if (st.c0 == 0 && j_of(st) == -1) {
-#pragma unroll
-            for (int a = 0; a < NTW; ++a)
-#pragma unroll
-                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.state_out + hst + so[a][q]) = hs[a][q];
-        }
+                hs[a][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * so[a][q], 0, 0));
     };
-    // End a unit (hs = h_{c1-1}): the final state when the unit ends the item.
-    auto end_unit = [&](const Step &st) __attribute__((always_inline)) {
-        if (st.c1 == nb && p.final_state) {
-            uint32_t so[NTW][PTW];
-            state_offsets(so);
-            const int64_t hst = (int64_t)st.item * P * N;
+    auto store_state = [&](float *base, const Step &st, const f32x4 (&v)[NTW][PTW])
+        __attribute__((always_inline)) {
+        const auto r = state_rows(base, st, true);
+        uint32_t so[NTW][PTW];
+        state_offsets(so);
 #pragma unroll
-            for (int a = 0; a < NTW; ++a)
+        for (int a = 0; a < NTW; ++a)
 #pragma unroll
-                for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(p.final_state + hst + so[a][q]) = hs[a][q];
-        }
+            for (int q = 0; q < PTW; ++q)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[a][q]), r, 4 * so[a][q], 0, 0);
     };
     auto dh_of = [&](const Step &st) {
         return p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[st.h] : 0.f;
@@ -635,12 +632,11 @@ void chunk_scan_fused_kernel(Params p) {
     // The state after an accepted index j in this step (position jl, 32-token
     // block mj), from the state entering the step (hs, before the step's
     // update): h_j = exp(cs_j) h_{c-1} + sum over tokens s <= j of B_s^T x_s
-    // with the exact factors exp2(cs2_j - ct_s), stored to state_out.  Runs
-    // at most once per item.
-    auto state_at_index = [&](const Step &st, const float *tb, int jl) __attribute__((always_inline)) {
+    // with the exact factors exp2(cs2_j - ct_s), into hv.  Runs at most once
+    // per item.
+    auto state_at_index = [&](const float *tb, int jl, f32x4 (&hv)[NTW][PTW]) __attribute__((always_inline)) {
         const int mj = jl / kStep;
         const float ej = exp2_hw(tb[TB_CS2 + jl]);
-        f32x4 hv[NTW][PTW];
 #pragma unroll
         for (int a = 0; a < NTW; ++a)
 #pragma unroll
@@ -668,13 +664,6 @@ void chunk_scan_fused_kernel(Params p) {
                 for (int a = 0; a < NTW; ++a) mma(fa[a], fb, hv[a][q]);
             }
         }
-        uint32_t so[NTW][PTW];
-        state_offsets(so);
-        float *dst = p.state_out + (int64_t)st.item * P * N;
-#pragma unroll
-        for (int a = 0; a < NTW; ++a)
-#pragma unroll
-            for (int q = 0; q < PTW; ++q) *reinterpret_cast<f32x4 *>(dst + so[a][q]) = hv[a][q];
     };
 
     // One step (tables in tb).  With the outputs (a full step): blue, then
@@ -689,9 +678,21 @@ void chunk_scan_fused_kernel(Params p) {
     // the end of its work (its rows meet the fewest blocks).
     auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
         __attribute__((always_inline)) {
-        if (full) {
-            const int64_t j = j_of(st);
-            if (j >= 0 && j / Q == st.c) state_at_index(st, tb, (int)(j - (int64_t)st.c * Q));
+        // A unit's first step: h_{-1} was loaded at the switch, before the
+        // TPL + UXR + UBR prefetch loads.  (Waiting here, on this path only,
+        // keeps the state's later uses free of waits on every other step.)
+        if (st.c == 0) wait_vmcnt<TPL + UXR + UBR>();
+        {
+            // state_out: the state after the accepted index j if j lies in
+            // this step, the initial state if j = -1 (in the item's first step).
+            const int64_t j = full ? j_of(st) : -2;
+            if (j >= 0 && j / Q == st.c) {
+                f32x4 hv[NTW][PTW];
+                state_at_index(tb, (int)(j - (int64_t)st.c * Q), hv);
+                store_state(p.state_out, st, hv);
+            } else if (j == -1 && st.c == 0) {
+                store_state(p.state_out, st, hs);
+            }
         }
         f32x4 acc[PT];
 #pragma unroll
@@ -731,6 +732,7 @@ void chunk_scan_fused_kernel(Params p) {
                 }
             }
         });
+        if (st.c + 1 == st.c1 && st.c1 == nb) store_state(p.final_state, st, hs);  // the item's last step
         load_c(nx, has_next && nx.c >= nx.c0);
         store_y(st, live, acc);
         if (has_next && wave == 0) make_tables(nx, tb_next);
@@ -747,7 +749,7 @@ void chunk_scan_fused_kernel(Params p) {
     wait_vmcnt<0>();
     if (wave == 0) make_tables(cur, tb0);
     lds_barrier();  // the tables are written
-    begin_unit(cur);
+    load_init(cur);
     enter(cur, tb0);
     {
         const Step nx = nsteps > 1 ? next_step(cur) : cur;
@@ -767,19 +769,19 @@ void chunk_scan_fused_kernel(Params p) {
         // stores or the next step's C rows issued after them: a wave's vector
         // memory operations complete in the order they were issued.
         wait_vmcnt<KS + PT / 2>();
-        if (cur.c + 1 == cur.c1) end_unit(cur);
-        if (has_next) {
-            lds_barrier();  // every wave has finished this step's LDS reads; next tables written
-            if (nx.c == 0) begin_unit(nx);
-            enter(nx, tbn);
-            const bool more = s + 2 < nsteps;
-            const Step nn = more ? next_step(nx) : nx;
-            load_dt(nn, more);  // first: see load_dt
-            load_x(nn, more);
-            load_b(nn, more);
-            lds_barrier();
-            cur = nx;
-        }
+        // The switch runs after the last step too (its loads then read
+        // nothing), so that every path round the loop issues the same memory
+        // operations and the compiler's count of loads in flight is exact.
+        lds_barrier();  // every wave has finished this step's LDS reads; next tables written
+        if (has_next && nx.c == 0) load_init(nx);
+        enter(nx, tbn);
+        const bool more = s + 2 < nsteps;
+        const Step nn = more ? next_step(nx) : nx;
+        load_dt(nn, more);  // first: see load_dt
+        load_x(nn, more);
+        load_b(nn, more);
+        lds_barrier();
+        cur = nx;
     }
 }
 
