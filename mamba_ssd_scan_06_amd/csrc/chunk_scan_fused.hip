@@ -471,16 +471,27 @@ void chunk_scan_fused_kernel(Params p) {
     // State loads and stores are rare (an item's first and last steps, and
     // the step holding its accepted index) and issued only where needed.
     // A unit starts from h_{-1}, the initial state (or 0), loaded at the
-    // switch into it.
+    // switch into it and waited for there: a load still in flight into the
+    // state on one path would make the compiler wait for every load in
+    // flight wherever the state is next used, on every path.
     auto load_init = [&](const Step &st) __attribute__((always_inline)) {
-        const auto r = state_rows(p.init_state, st, true);
-        uint32_t so[NTW][PTW];
-        state_offsets(so);
+        if (p.init_state) {
+            const auto r = state_rows(p.init_state, st, true);
+            uint32_t so[NTW][PTW];
+            state_offsets(so);
 #pragma unroll
-        for (int a = 0; a < NTW; ++a)
+            for (int a = 0; a < NTW; ++a)
 #pragma unroll
-            for (int q = 0; q < PTW; ++q)
-                hs[a][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * so[a][q], 0, 0));
+                for (int q = 0; q < PTW; ++q)
+                    hs[a][q] =
+                        __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * so[a][q], 0, 0));
+            wait_vmcnt<0>();
+        } else {
+#pragma unroll
+            for (int a = 0; a < NTW; ++a)
+#pragma unroll
+                for (int q = 0; q < PTW; ++q) hs[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     };
     auto store_state = [&](float *base, const Step &st, const f32x4 (&v)[NTW][PTW])
         __attribute__((always_inline)) {
@@ -678,10 +689,13 @@ void chunk_scan_fused_kernel(Params p) {
     // the end of its work (its rows meet the fewest blocks).
     auto compute = [&](const Step &st, bool has_next, const Step &nx, const float *tb, float *tb_next)
         __attribute__((always_inline)) {
-        // A unit's first step: h_{-1} was loaded at the switch, before the
-        // TPL + UXR + UBR prefetch loads.  (Waiting here, on this path only,
-        // keeps the state's later uses free of waits on every other step.)
-        if (st.c == 0) wait_vmcnt<TPL + UXR + UBR>();
+        // The next step's dt (for its tables, made at the end of this step)
+        // and its x and B rows (written to LDS at the switch): issued here,
+        // outside the switch, so that no wave waits at a barrier for their
+        // issue, and a whole step covers their latency.
+        load_dt(nx, has_next);  // first: see load_dt
+        load_x(nx, has_next);
+        load_b(nx, has_next);
         {
             // state_out: the state after the accepted index j if j lies in
             // this step, the initial state if j = -1 (in the item's first step).
@@ -739,8 +753,8 @@ void chunk_scan_fused_kernel(Params p) {
     };
 
     // ---- prologue: the first step's inputs and tables.  The tables of
-    // step s are in tb0 / tb1 for s even / odd, made by wave 0 at the start
-    // of step s - 1 from the dt values fetched at the switch into it.
+    // step s are in tb0 / tb1 for s even / odd, made by wave 0 at the end
+    // of step s - 1 from the dt values fetched at its start.
     Step cur = step_of(0);
     load_dt(cur, true);
     load_x(cur, true);
@@ -751,12 +765,6 @@ void chunk_scan_fused_kernel(Params p) {
     lds_barrier();  // the tables are written
     load_init(cur);
     enter(cur, tb0);
-    {
-        const Step nx = nsteps > 1 ? next_step(cur) : cur;
-        load_dt(nx, nsteps > 1);
-        load_x(nx, nsteps > 1);
-        load_b(nx, nsteps > 1);
-    }
     lds_barrier();
 
     // ---- steps.
@@ -769,17 +777,12 @@ void chunk_scan_fused_kernel(Params p) {
         // stores or the next step's C rows issued after them: a wave's vector
         // memory operations complete in the order they were issued.
         wait_vmcnt<KS + PT / 2>();
-        // The switch runs after the last step too (its loads then read
-        // nothing), so that every path round the loop issues the same memory
+        // The switch runs after the last step too (nothing was loaded for
+        // it), so that every path round the loop issues the same memory
         // operations and the compiler's count of loads in flight is exact.
         lds_barrier();  // every wave has finished this step's LDS reads; next tables written
         if (has_next && nx.c == 0) load_init(nx);
         enter(nx, tbn);
-        const bool more = s + 2 < nsteps;
-        const Step nn = more ? next_step(nx) : nx;
-        load_dt(nn, more);  // first: see load_dt
-        load_x(nn, more);
-        load_b(nn, more);
         lds_barrier();
         cur = nx;
     }
