@@ -610,33 +610,50 @@ void chunk_scan_fused_kernel(Params p) {
     // on = false every store is dropped).  y is written once and not read
     // here: non-temporal stores keep it from displacing the B and C rows the
     // other heads still read.  Lane (il, grp) holds channels 16q + 4grp .. +3
-    // of row il; the four lanes of a row swap values so that lane g holds
-    // channels 32k + 8g .. +7 for k < PT/2 and each store writes 64
-    // contiguous bytes of every row.
+    // of row il; the four lanes of a row swap values (through the LDS
+    // permute) so that lane g holds the 16-byte pieces g and 4 + g (channels
+    // 8g .. +7 and 32 + 8g .. +7) of row il.  With 64 channels, lanes il and
+    // il ^ 8 then swap one piece (a DPP row rotation) so that each of the two
+    // stores writes 8 whole 128-byte rows: partial lines would cost the
+    // memory a read-modify-write.
     auto store_y = [&](const Step &st, bool on, const f32x4 (&acc)[PT]) __attribute__((always_inline)) {
-        {
-            const auto r = y_rows(st, on);
-            int ln = lane;  // opaque: the shuffle sources are recomputed here
-            asm volatile("" : "+v"(ln));
-            const int g = ln >> 4, s0 = ((ln & 15) + 32 * (g & 1)) << 2, s1 = s0 + 64;
-            u32x2 o[PT];
+        const auto r = y_rows(st, on);
+        int ln = lane;  // opaque: the shuffle sources are recomputed here
+        asm volatile("" : "+v"(ln));
+        const int g = ln >> 4, s0 = ((ln & 15) + 32 * (g & 1)) << 2, s1 = s0 + 64;
+        u32x2 o[PT];
 #pragma unroll
-            for (int q = 0; q < PT; ++q)
-                o[q] = __builtin_bit_cast(u32x2, V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]});
+        for (int q = 0; q < PT; ++q)
+            o[q] = __builtin_bit_cast(u32x2, V4{(T)acc[q][0], (T)acc[q][1], (T)acc[q][2], (T)acc[q][3]});
+        u32x4 d[PT / 2];  // d[k]: piece 4k + g of row il
+#pragma unroll
+        for (int k = 0; k < PT / 2; ++k) {
+            u32x4 w[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {  // channels 16(2k + j) + 4grp' .., grp' = 2(g & 1) and 2(g & 1) + 1
+                const u32x2 v = o[2 * k + j];
+                w[j] = u32x4{(unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[0]),
+                             (unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[1]),
+                             (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[0]),
+                             (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[1])};
+            }
+            d[k] = (g >> 1) ? w[1] : w[0];
+        }
+        if constexpr (PT == 4) {
+            const bool lo = (ln & 8) == 0;
+            const u32x4 x = lo ? d[1] : d[0];
+            u32x4 rcv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)  // row_ror:8 within each row of 16 lanes: lane il ^ 8
+                rcv[e] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)x[e], 0x128, 0xf, 0xf, false);
+            // lane (il, g) writes piece g + 4 (il >> 3) of rows (il & 7) and (il & 7) + 8
+            const uint32_t vy = (uint32_t)(16 * tile + (ln & 7)) * HP2 + 16 * (g + 4 * ((ln >> 3) & 1));
+            __builtin_amdgcn_raw_buffer_store_b128(lo ? d[0] : rcv, r, vy, 0, kAuxNt);
+            __builtin_amdgcn_raw_buffer_store_b128(lo ? rcv : d[1], r, vy + 8 * HP2, 0, kAuxNt);
+        } else {
             const uint32_t vyr = (uint32_t)(16 * tile + (ln & 15)) * HP2 + 16 * g;
 #pragma unroll
-            for (int k = 0; k < PT / 2; ++k) {
-                u32x4 w[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {  // channels 16(2k + j) + 4grp' .., grp' = 2(g & 1) and 2(g & 1) + 1
-                    const u32x2 v = o[2 * k + j];
-                    w[j] = u32x4{(unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[0]),
-                                 (unsigned)__builtin_amdgcn_ds_bpermute(s0, (int)v[1]),
-                                 (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[0]),
-                                 (unsigned)__builtin_amdgcn_ds_bpermute(s1, (int)v[1])};
-                }
-                __builtin_amdgcn_raw_buffer_store_b128((g >> 1) ? w[1] : w[0], r, vyr + 64 * k, 0, kAuxNt);
-            }
+            for (int k = 0; k < PT / 2; ++k) __builtin_amdgcn_raw_buffer_store_b128(d[k], r, vyr + 64 * k, 0, kAuxNt);
         }
     };
 
