@@ -11,10 +11,12 @@ bf16 in, fp32 state, zero initial state); the other four workloads are timed
 too and reported under "workloads".  Prints ONE JSON line.
 
 Timing has one source: HIP events recorded on the stream the library's
-kernels run on (torch's current stream, which the binding passes down), one
-before every step and one after the last.  "value" and "ms_per_step" are the
-K steps back to back (warm: whatever the 256 MB last-level cache keeps
-between steps).  The cold figures time single steps, each after a 512 MiB
+kernels run on (torch's current stream, which the binding passes down).
+"value" and "ms_per_step" are the K steps back to back between the first
+and the last event (warm: whatever the 256 MB last-level cache keeps between
+steps); events also close each of up to 10 groups of those steps, whose means
+give the warm median and min (an event between every two steps would add its
+own gap to each).  The cold figures time single steps, each after a 512 MiB
 buffer is written on the same stream, which evicts the caches.
 
 The roofline entry is for the dominant kernel.  On the automatic path the
@@ -142,10 +144,10 @@ def device_inputs(inp, device):
                 state_out_idx=t(inp.state_out_idx))
 
 
-def _stats(us):
+def _stats(us, n_steps=None):
     s = sorted(us)
     return {"mean_us": round(sum(s) / len(s), 2), "median_us": round(s[len(s) // 2], 2), "min_us": round(s[0], 2),
-            "max_us": round(s[-1], 2), "steps": len(s)}
+            "max_us": round(s[-1], 2), "samples": len(s), "steps": n_steps or len(s)}
 
 
 FLUSH_BYTES = 512 << 20
@@ -182,17 +184,22 @@ def time_workload(wl, steps, warmup, device, path_name="auto", cold_steps=10):
     for _ in range(warmup):
         ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
     torch.cuda.synchronize()
-    # Warm: K steps back to back, an event before each and after the last.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # Warm: K steps back to back in `blocks` groups, an event before the first
+    # step and after each group (an event between every two steps would add
+    # its own gap to each); the median and min are over the groups' means.
+    blocks = max(1, min(10, steps // 10))
+    bounds = [steps * g // blocks for g in range(blocks + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
     t0 = time.perf_counter()
     evs[0].record()
-    for k in range(steps):
-        ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
-        evs[k + 1].record()
+    for g in range(blocks):
+        for _ in range(bounds[g], bounds[g + 1]):
+            ssd.ssd_chunk_scan_fwd_ex(*args, **kw)
+        evs[g + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    warm_us = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)]
-    ms_step = evs[0].elapsed_time(evs[steps]) / steps
+    warm_us = [evs[g].elapsed_time(evs[g + 1]) * 1e3 / (bounds[g + 1] - bounds[g]) for g in range(blocks)]
+    ms_step = evs[0].elapsed_time(evs[blocks]) / steps
     # Cold: each step after 512 MiB are written on the same stream.
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cold_steps)]
@@ -204,7 +211,8 @@ def time_workload(wl, steps, warmup, device, path_name="auto", cold_steps=10):
     torch.cuda.synchronize()
     cold_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
     del flush
-    return inp, dict(ms_per_step=ms_step, wall_s=wall, warm=_stats(warm_us), cold=_stats(cold_us),
+    warm = dict(_stats(warm_us, steps), mean_us=round(ms_step * 1e3, 2))
+    return inp, dict(ms_per_step=ms_step, wall_s=wall, warm=warm, cold=_stats(cold_us),
                      kernels=names, path=ssd.PATH_NAMES[run_path])
 
 
@@ -347,7 +355,11 @@ def _read_csv(pattern):
     return files, rows
 
 
-def summarize_stats(d, workload=HEADLINE, command=""):
+def summarize_stats(d, workload=HEADLINE, command="", steps=None, warmup=None, cold_steps=None):
+    """The rocprofv3 kernel statistics of a bench.py run, and for each kernel
+    launched once per step, its mean and median duration over the timed
+    steps alone (bench.py launches one marked step, then `warmup` steps,
+    then the `steps` timed ones, then `cold_steps` after cache flushes)."""
     files, rows = _read_csv(os.path.join(d, "**", "*kernel_stats.csv"))
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -358,6 +370,22 @@ def summarize_stats(d, workload=HEADLINE, command=""):
         short = (name[:name.rfind("(")] if name.endswith(")") else name)[-90:]
         lines.append(f"{short} | {r.get('Calls')} | {r.get('TotalDurationNs')} | {float(r.get('AverageNs', 0)):.0f} | "
                      f"{r.get('MinNs')} | {r.get('MaxNs')} | {float(r.get('Percentage', 0)):.2f}")
+    _, trace = _read_csv(os.path.join(d, "**", "*kernel_trace.csv"))
+    if trace and steps is not None and warmup is not None:
+        per = {}
+        for r in trace:
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        n_expected = 1 + warmup + steps + (cold_steps or 0)
+        lines.append(f"# timed steps only (dispatches {1 + warmup} .. {warmup + steps} of each step kernel, "
+                     f"in launch order): name | steps | mean_ns | median_ns")
+        for name, ds in per.items():
+            if len(ds) != n_expected:
+                continue
+            ds.sort()
+            t = sorted(v for _, v in ds[1 + warmup:1 + warmup + steps])
+            short = (name[:name.rfind("(")] if name.endswith(")") else name)[-90:]
+            lines.append(f"timed | {short} | {len(t)} | {sum(t) / len(t):.0f} | {t[len(t) // 2]}")
     out = os.path.join(PROFILES, f"kernels_{workload}_kernel_stats.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -437,7 +465,9 @@ def summarize_pmc(dirs, workload=HEADLINE, commands=()):
                       f"traffic_bytes_per_launch = {fb + wb:.0f}"]
             if ab:
                 lines += [f"algorithmic_bytes_per_launch = {ab}", f"traffic_over_algorithmic = {(fb + wb) / ab:.3f}"]
-        if c.get("SQ_INSTS_MFMA") is not None:
+        if c.get("SQ_INSTS_MFMA") == 0:
+            lines.append("# no MFMA instructions: this kernel computes on the vector ALUs")
+        elif c.get("SQ_INSTS_MFMA") is not None:
             ex = c["SQ_INSTS_MFMA"] * MFMA_FLOPS[wl.dtype]
             lines += [f"# executed MFMA flops = SQ_INSTS_MFMA x {MFMA_FLOPS[wl.dtype]} flops per instruction",
                       f"mfma_flops_executed = {ex:.0f}"]
@@ -481,7 +511,8 @@ def main():
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc, workload=args.workload, commands=args.command)
     if args.summarize_stats:
-        return summarize_stats(args.summarize_stats, workload=args.workload, command=" ".join(args.command))
+        return summarize_stats(args.summarize_stats, workload=args.workload, command=" ".join(args.command),
+                               steps=args.steps, warmup=args.warmup, cold_steps=args.cold_steps)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SSD forward here runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
@@ -536,7 +567,9 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "alg_flops_per_step": flops,
-        "timing": {"source": "HIP events on the library's stream, one before each step and one after the last",
+        "timing": {"source": "HIP events on the library's stream: warm, one before the first step and one after "
+                             "each of up to 10 groups of back-to-back steps (mean over all steps; median and min "
+                             "over the groups' means); cold, one pair around each step after a 512 MiB flush",
                    "warm": res["warm"], "cold": dict(res["cold"], flush_bytes=FLUSH_BYTES),
                    "wall_s": round(res["wall_s"], 4)},
         "roofline": roofline_entry(wl, res),
