@@ -580,21 +580,21 @@ void chunk_scan_fused_kernel(Params p) {
     // skip term), rounded to bf16 once (applied to raw x).  j - i = 16 half +
     // r - di, with di from an opaque copy so that the comparisons are made
     // here and not kept across the loop.
-    auto orange_diag = [&](const float *tb, float cs2i, float dh) __attribute__((always_inline)) {
-        int di = 16 * (tile & 1) + il - 4 * grp;
+    auto orange_diag = [&](const float *tb, float cs2i, float dh, int mdo, int todd) __attribute__((always_inline)) {
+        int di = 16 * todd + il - 4 * grp;
         asm volatile("" : "+v"(di));
         f32x4 ct0, ct1;
-        slot_pair(tb + TB_CT, md, ct0, ct1);
+        slot_pair(tb + TB_CT, mdo, ct0, ct1);
         Frag<T> lf;
-        const f32x4 g0 = g_half(md, 0);
+        const f32x4 g0 = g_half(mdo, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             // above the diagonal the factor may overflow; the select drops it
             const float v = r > di ? 0.f : g0[r] * exp2_hw(cs2i - ct0[r]);
             lf.set(r, r == di ? v + dh : v);
         }
-        if (tile & 1) {
-            const f32x4 g1 = g_half(md, 1);
+        if (todd) {
+            const f32x4 g1 = g_half(mdo, 1);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = 16 + r > di ? 0.f : g1[r] * exp2_hw(cs2i - ct1[r]);
@@ -731,6 +731,11 @@ void chunk_scan_fused_kernel(Params p) {
         const float cs2i = tb[TB_CS2 + 16 * tile + il];
         const float dh = dh_of(st);
         if (live && (st.c > 0 || p.init_state != nullptr)) blue(cs2i, acc);
+        // md and the tile's parity from opaque copies: the compiler would
+        // otherwise hoist every comparison with them out of the loop as a
+        // 64-bit lane mask and keep (spill) them all.
+        int mdo = md, todd = tile & 1;
+        asm volatile("" : "+s"(mdo), "+s"(todd));
         const float gl = exp2_hw(ce[NBLK - 1]);  // exp(cs_last)
 #pragma unroll
         for (int a = 0; a < NTW; ++a)
@@ -739,10 +744,10 @@ void chunk_scan_fused_kernel(Params p) {
         static_for<NBLK>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
             if (m >= nblk) return;
-            const bool orange = live && m <= md;
+            const bool orange = live && m <= mdo;
             Frag<T> of;
-            if (live && m < md) of = orange_below(m, tb, cs2i);
-            if (live && m == md) of = orange_diag(tb, cs2i, dh);
+            if (live && m < mdo) of = orange_below(m, tb, cs2i);
+            if (live && m == mdo) of = orange_diag(tb, cs2i, dh, mdo, todd);
             Frag<T> fa[NTW];
 #pragma unroll
             for (int a = 0; a < NTW; ++a) fa[a] = read_tr(bl + bT + kStep * m * SB + 32 * a, 16 * SB);
