@@ -15,13 +15,13 @@
 //
 // Block c (tokens t0 .. t0+Qc-1), head h of group g; cs the block-local
 // inclusive cumulative log-decay A_h sum dt, cs2 = cs log2(e),
-// ct_j = cs2_j - log2(dt_j), e(m) the last token of 32-token block m and
-// dte_j = dt_j exp(cs_e(m) - cs_j) for j in m (all computed per block by one
-// wave, in fp64 and rounded once):
+// ct_j = cs2_j - log2(dt_j), e(m) the last token of 32-token block m,
+// dte_j = dt_j exp(cs_e(m) - cs_j) for j in m and wl_j = dt_j exp(cs_last -
+// cs_j) (all computed per block by one wave, in fp64 and rounded once):
 //   G      = C B^T (causal 16x32 tiles, fp32 accumulate)
 //   orange y_i  = sum_{j<=i} exp(cs_i - cs_j) dt_j G_ij x_j
 //   blue   y_i += exp(cs_i) C_i . h_{c-1}
-//   green  h_c  = exp(cs_last) h_{c-1} + sum_j exp(cs_last - cs_j) dt_j x_j B_j^T
+//   green  h_c  = exp(cs_last) h_{c-1} + sum_j wl_j B_j^T x_j
 //          y_i += D_h x_i.
 // Decay factors.  Every factor applied is at most max(1, dt):
 //   orange, block m below the tile's diagonal block md: G_ij times
@@ -30,9 +30,9 @@
 //     (selected to 0 above the diagonal), plus D at j = i, rounded
 //     once, on raw x; exact however strong the decay inside the block;
 //   blue: exp2(cs2_i) times C_i . h_{c-1};
-//   state, in Horner form over the 32-token blocks: acc = acc g_m +
-//     (dte B)_m^T x_m with g_0 = exp(cs_e(0)), g_m = exp(cs_e(m) - cs_e(m-1));
-//     dte B is formed from the transposed B fragment and rounded once.
+//   state: the state scaled once per block by exp(cs_last), plus the
+//     products of the B fragments weighted by wl (formed from the
+//     transposed B read and rounded once) with raw x.
 // The state after an accepted index j (multi-step verify, "3天把Llama训成
 // Mamba", blog.csdn.net, section "推测解码") is computed in the block holding
 // j, from the state entering it, with the exact factors exp2(cs2_j - ct_s):
@@ -43,18 +43,20 @@
 // and own their columns of x and y and their rows of the state.
 //
 // Work split inside a workgroup: 8 waves, each owning one 16-row tile of
-// the block (tiles dealt so that both waves of a SIMD meet 3 off-diagonal
-// 32-token blocks together) and NTW x PTW 16x16 tiles of the state.  LDS
-// holds the block's B rows and x rows (token-major, read with the
-// transposing LDS read), h_{c-1} in bf16 and the per-token tables.  Under
-// 80 KB at dstate 128, so two workgroups share a compute unit and one's
-// block switch overlaps the other's products.  While block c computes,
-// block c+1's x and B rows are loaded into registers and its dt values
-// fetched (wave 0 turns them into block c+1's tables); its C rows follow
-// once block c no longer needs them.  At the switch every wave waits for
-// its loads and writes the next block's LDS, and one barrier publishes
-// them.  Global accesses go through buffer descriptors over each block's
-// rows (rows past the sequence read as zero, their stores are dropped).
+// the block (tiles dealt so that the two waves of a SIMD meet 3 off-diagonal
+// 32-token blocks together) and the state tiles of one n tile.  Per block a
+// wave computes blue, then walks the 32-token blocks m once: each block's x
+// fragments (transposing LDS read) feed both its orange product (m <= md)
+// and its state update.  LDS holds the block's B rows and x rows
+// (token-major, read with the transposing LDS read), h_{c-1} in bf16 and the
+// per-token tables (two copies: wave 0 writes the next block's while this
+// block's are read).  Under 80 KB at dstate 128, so two workgroups share a
+// compute unit and one's block switch overlaps the other's products.  The
+// next block's x and B rows are loaded into registers at the start of a
+// block, its dt values and C rows after the block's last use of C; at the
+// switch every wave writes the next block's LDS and one barrier publishes
+// it.  Global accesses go through buffer descriptors over each block's rows
+// (rows past the sequence read as zero, their stores are dropped).
 //
 // Schedule: a grid of two workgroups per compute unit; workgroup w runs on
 // XCD w mod 8 (the hardware deals workgroups to the XCDs in turn), and each

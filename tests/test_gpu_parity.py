@@ -413,6 +413,27 @@ def test_fused_degenerate_values(zero_dt, zero_A):
         check(k, got[k], ref[k], TOL["bf16"])
 
 
+# dstate 256 with at most 64 items (the long-sequence configuration's
+# geometry at shorter lengths): these take the chunk-parallel path.
+N256 = [
+    # b, T, H, P, N, G, Q, init_state, state_out
+    (1, 2500, 64, 64, 256, 1, 256, True, True),    # 64 items, 10 chunks, last partial
+    (2, 1300, 16, 64, 256, 2, 128, False, True),   # 32 items, zero start
+    (1, 777, 8, 128, 256, 1, 256, True, False),    # headdim 128, 8 heads
+]
+
+
+@pytest.mark.parametrize("case", N256, ids=lambda c: "b{}_T{}_H{}_P{}_N{}_G{}_Q{}_init{}_sout{}".format(*c))
+def test_dstate_256(case):
+    b, T, H, P, N, G, Q, init, sout = case
+    wl = workload("n256", b, T, H, P, N, G, Q, "bf16", init_state=init, state_out=sout, seed=261 + T)
+    announce(f"dstate 256 {wl}")
+    inp = ssd_inputs.generate(wl)
+    got, ref = gpu_run(inp), oracle_run(inp)
+    for k in ("y", "final") + (("state_out",) if sout else ()):
+        check(k, got[k], ref[k], TOL["bf16"])
+
+
 def test_paths_agree_at_layer_shape():
     # The 2.7B layer's shape (fewer tokens) through the single pass and the
     # chunk-parallel kernels, each against the oracle.
