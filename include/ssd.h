@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -139,8 +139,9 @@ int ssd_select_path(const ssd_shape *shape, int chunk_size, ssd_dtype dtype);
  *            so that dt_j exp(cs_i - cs_j) = exp2(cs_i log2(e) - ct_j).
  *   dt_decay fp32, same layout: dt_i * exp(cs_e - cs_i), e = the last token
  *            (within seqlen) of the 32-token block holding i.
- *   states   fp32 [batch, nchunks, nheads, headdim, dstate]: entry c is the
- *            state chunk c reaches from a zero initial state.
+ *   states   dtype [batch, nchunks, nheads, headdim, dstate]: entry c is the
+ *            state chunk c reaches from a zero initial state (accumulated in
+ *            fp32, rounded to nearest even to dtype once).
  *   prev     dtype, same layout: entry c is the state entering chunk c,
  *            rounded to nearest even to dtype; entry 0 is written only when
  *            init_state is given (otherwise it is never read).

@@ -280,8 +280,8 @@ def _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_stat
 def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
     """Views into the chunk-parallel path's workspace after a call, by the
     layout of include/ssd.h: cs, ct and dte [b,H,nc,Q] fp32, the chunk states
-    from a zero start [b,nc,H,P,N] fp32, and the states entering each chunk
-    [b,nc,H,P,N] in the input dtype (entry 0 only with init_state)."""
+    from a zero start and the states entering each chunk (entry 0 only with
+    init_state), both [b,nc,H,P,N] in the input dtype."""
     import torch
 
     lay = ssd_get_workspace_layout(shape, chunk_size, dtype)
@@ -298,5 +298,5 @@ def workspace_views(workspace, shape: ssd_shape, chunk_size: int, dtype: int):
     return dict(cs=region(lay.cumsum_offset, 4 * n_cs, torch.float32, tab),
                 ct=region(lay.ct_offset, 4 * n_cs, torch.float32, tab),
                 dte=region(lay.dt_decay_offset, 4 * n_cs, torch.float32, tab),
-                states=region(lay.states_offset, 4 * n_st, torch.float32, (b, nc, H, P, N)),
+                states=region(lay.states_offset, esz * n_st, tdt, (b, nc, H, P, N)),
                 prev=region(lay.prev_offset, esz * n_st, tdt, (b, nc, H, P, N)))

@@ -207,7 +207,11 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(Params p, bool at_inde
                 v = v + e_last * hp;
                 *reinterpret_cast<f32x4 *>(p.state_out + at) = v;
             } else {
-                *reinterpret_cast<f32x4 *>(p.states + state_base + (int64_t)pp * N + n) = v;
+                T *sd = reinterpret_cast<T *>(p.states) + state_base + (int64_t)pp * N + n;
+                if constexpr (sizeof(T) == 2)
+                    *reinterpret_cast<bf16x4 *>(sd) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                else
+                    *reinterpret_cast<f32x4 *>(sd) = v;
             }
         }
     }

@@ -198,13 +198,14 @@ __global__ __launch_bounds__(64 * kWaves) void chunk_state_heads_kernel(Params p
         }
         // acc[a][q][r] = S^T[n = 16*(nw*NTW + a) + 4*grp + r][p = 16*(pw*PTW + q) + il]
         const int h = hbeg + hh;
-        float *sd = p.states + ((b * nc + c) * H + h) * (int64_t)P * N;
+        bf16 *sd = reinterpret_cast<bf16 *>(p.states) + ((b * nc + c) * H + h) * (int64_t)P * N;
 #pragma unroll
         for (int a = 0; a < NTW; ++a)
 #pragma unroll
             for (int q = 0; q < PTW; ++q) {
                 const int n = 16 * (nw * NTW + a) + 4 * grp, pp = 16 * (pw * PTW + q) + il;
-                *reinterpret_cast<f32x4 *>(sd + (int64_t)pp * N + n) = acc[a][q];
+                const f32x4 v = acc[a][q];
+                *reinterpret_cast<bf16x4 *>(sd + (int64_t)pp * N + n) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
             }
     };
 

@@ -27,7 +27,8 @@ struct Params {
     float *cs;                // workspace [b,H,nc,Q]: chunk-local cumulative log-decay
     float *ct;                // workspace [b,H,nc,Q]: cs * log2(e) - log2(dt) (+inf past the end)
     float *dte;               // workspace [b,H,nc,Q]: dt_i * exp(cs_e - cs_i), e = last token of i's 32-token block
-    float *states;            // workspace [b,nc,H,P,N] fp32: chunk states S_c (from a zero start)
+    void *states;             // workspace [b,nc,H,P,N] T_elem: chunk states S_c (from a zero start),
+                              // rounded once to the input type
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
     float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
     int64_t batch, seqlen;

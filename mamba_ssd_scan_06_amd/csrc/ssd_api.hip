@@ -92,7 +92,7 @@ Layout layout_of(const ssd_shape *s, int chunk, ssd_dtype dtype) {
     L.ct_off = tab_bytes;
     L.dte_off = 2 * tab_bytes;
     L.st_off = 3 * tab_bytes;
-    L.prev_off = L.st_off + round_up(n_st * sizeof(float));
+    L.prev_off = L.st_off + round_up(n_st * esz);
     L.hj_off = L.prev_off + round_up(n_st * esz);
     L.total = L.nc > 0 && s->batch > 0 ? L.hj_off + round_up(n_hj * sizeof(float)) : 0;
     return L;
@@ -339,7 +339,7 @@ ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
     p.cs = ws ? reinterpret_cast<float *>(ws + L.cs_off) : nullptr;
     p.ct = ws ? reinterpret_cast<float *>(ws + L.ct_off) : nullptr;
     p.dte = ws ? reinterpret_cast<float *>(ws + L.dte_off) : nullptr;
-    p.states = ws ? reinterpret_cast<float *>(ws + L.st_off) : nullptr;
+    p.states = ws ? static_cast<void *>(ws + L.st_off) : nullptr;
     p.prev = ws ? static_cast<void *>(ws + L.prev_off) : nullptr;
     p.hj = ws && state_out ? reinterpret_cast<float *>(ws + L.hj_off) : nullptr;
     p.no_split = in_place ? 1 : 0;

@@ -16,7 +16,8 @@
 //             the state at that index is requested (the initial state when
 //             that index is -1);
 //   final_state = h_{nc-1}.
-// The chunk states themselves are left as they are.
+// The chunk states (in the input type: one rounding of each S_c) are left as
+// they are.
 //
 // One lane per four consecutive state elements (b, h, p, n..n+3): 16-byte
 // coalesced loads, sequential over chunks.  The chunk states of a batch of
@@ -42,6 +43,18 @@ __device__ inline void store4<bf16>(bf16 *dst, const f32x4 &v) {
 }
 
 template <typename T>
+__device__ inline f32x4 load4(const T *src);
+template <>
+__device__ inline f32x4 load4<float>(const float *src) {
+    return *reinterpret_cast<const f32x4 *>(src);
+}
+template <>
+__device__ inline f32x4 load4<bf16>(const bf16 *src) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <typename T>
 __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
     const int64_t pn4 = (int64_t)p.headdim * p.dstate / 4;
     const int64_t per_b = (int64_t)p.nheads * pn4;
@@ -58,7 +71,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
     const float *cs_last = p.cs + (b * H + h) * (int64_t)nc * Q + (Q - 1);
     const int64_t first = (b * nc * H + h) * pn4 + q;  // chunk 0's element, in units of 4
     const int64_t stride = (int64_t)H * pn4;           // one chunk further
-    const f32x4 *st = reinterpret_cast<const f32x4 *>(p.states) + first;
+    const T *st = reinterpret_cast<const T *>(p.states) + 4 * first;
     T *prev = reinterpret_cast<T *>(p.prev) + 4 * first;
     int cj = -2;  // chunk whose entering state the state-at-index step reads
     if (p.hj && p.state_out_idx) {
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             if (c0 + k < nc) {
-                s[k] = st[(c0 + k) * stride];
+                s[k] = load4<T>(st + 4 * (c0 + k) * stride);
                 a[k] = exp_neg(cs_last[(int64_t)(c0 + k) * Q]);
             }
         }

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ssd.ssd_abi_version() == 6
+    assert ssd.ssd_abi_version() == 7
 
 
 def test_status_strings():
@@ -58,7 +58,7 @@ def test_workspace_bytes_formula():
     assert lay.nchunks == nc and lay.cumsum_offset == 0
     assert lay.ct_offset == rnd(tab) and lay.dt_decay_offset == 2 * rnd(tab)
     assert lay.states_offset == 3 * rnd(tab)
-    assert lay.prev_offset == lay.states_offset + rnd(4 * n_st)
+    assert lay.prev_offset == lay.states_offset + rnd(2 * n_st)   # bf16 chunk states
     assert lay.hj_offset == lay.prev_offset + rnd(2 * n_st)
     assert lay.total_bytes == lay.hj_offset + rnd(4 * n_hj)
     assert ssd.ssd_workspace_bytes(s, 64, ssd.SSD_DTYPE_BF16) == lay.total_bytes
