@@ -19,10 +19,11 @@
 // The chunk states (in the input type: one rounding of each S_c) are left as
 // they are.
 //
-// One lane per four consecutive state elements (b, h, p, n..n+3): 16-byte
-// coalesced loads, sequential over chunks.  The chunk states of a batch of
-// chunks are loaded before any result is stored so that the loads are in
-// flight together.
+// One lane per 16 bytes of consecutive state elements (b, h, p, n..n+E-1;
+// E = 8 for bf16 chunk states, 4 for fp32), sequential over chunks.  The
+// chunk states are loaded in batches of kBatchChunks chunks, and the loads of
+// the next batch are issued before the current one is combined, so that two
+// batches of loads per lane are in flight.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -31,79 +32,106 @@ namespace {
 
 constexpr int kBatchChunks = 8;
 
-template <typename T>
-__device__ inline void store4(T *dst, const f32x4 &v);
-template <>
-__device__ inline void store4<float>(float *dst, const f32x4 &v) {
-    *reinterpret_cast<f32x4 *>(dst) = v;
-}
-template <>
-__device__ inline void store4<bf16>(bf16 *dst, const f32x4 &v) {
-    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
+// E consecutive elements of one lane, held in fp32.
+template <int E> struct Lane { f32x4 v[E / 4]; };
+// ... and as loaded (16 bytes in the chunk states' type).
+template <typename T> struct Raw16 { typedef bf16x8 type; };
+template <> struct Raw16<float> { typedef f32x4 type; };
 
-template <typename T>
-__device__ inline f32x4 load4(const T *src);
-template <>
-__device__ inline f32x4 load4<float>(const float *src) {
-    return *reinterpret_cast<const f32x4 *>(src);
+template <typename T, int E>
+__device__ inline Lane<E> widen(const typename Raw16<T>::type &w) {
+    Lane<E> r;
+    if constexpr (sizeof(T) == 2) {
+        r.v[0] = f32x4{(float)w[0], (float)w[1], (float)w[2], (float)w[3]};
+        r.v[1] = f32x4{(float)w[4], (float)w[5], (float)w[6], (float)w[7]};
+    } else {
+        r.v[0] = w;
+    }
+    return r;
 }
-template <>
-__device__ inline f32x4 load4<bf16>(const bf16 *src) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+template <typename T, int E>
+__device__ inline void store_lane(T *dst, const Lane<E> &x) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x8 *>(dst) = bf16x8{(bf16)x.v[0][0], (bf16)x.v[0][1], (bf16)x.v[0][2], (bf16)x.v[0][3],
+                                                  (bf16)x.v[1][0], (bf16)x.v[1][1], (bf16)x.v[1][2], (bf16)x.v[1][3]};
+    } else {
+        *reinterpret_cast<f32x4 *>(dst) = x.v[0];
+    }
+}
+template <int E>
+__device__ inline void store_f32(float *dst, const Lane<E> &x) {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) reinterpret_cast<f32x4 *>(dst)[i] = x.v[i];
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
-    const int64_t pn4 = (int64_t)p.headdim * p.dstate / 4;
-    const int64_t per_b = (int64_t)p.nheads * pn4;
+    constexpr int E = 16 / (int)sizeof(T);
+    typedef Lane<E> LaneT;
+    const int64_t pne = (int64_t)p.headdim * p.dstate / E;  // lanes per (b, h)
+    const int64_t per_b = (int64_t)p.nheads * pne;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= p.batch * per_b) return;
     const int64_t b = e / per_b;
     const int64_t rem = e - b * per_b;
-    const int64_t h = rem / pn4;
-    const int64_t q = rem - h * pn4;
+    const int64_t h = rem / pne;
+    const int64_t q = rem - h * pne;
     const int H = p.nheads, nc = p.nchunks, Q = p.chunk;
 
-    f32x4 hc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (p.init_state) hc = reinterpret_cast<const f32x4 *>(p.init_state)[e];
+    LaneT hc;
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i)
+        hc.v[i] = p.init_state ? reinterpret_cast<const f32x4 *>(p.init_state)[e * (E / 4) + i] : f32x4{0.f, 0.f, 0.f, 0.f};
     const float *cs_last = p.cs + (b * H + h) * (int64_t)nc * Q + (Q - 1);
-    const int64_t first = (b * nc * H + h) * pn4 + q;  // chunk 0's element, in units of 4
-    const int64_t stride = (int64_t)H * pn4;           // one chunk further
-    const T *st = reinterpret_cast<const T *>(p.states) + 4 * first;
-    T *prev = reinterpret_cast<T *>(p.prev) + 4 * first;
+    const int64_t first = ((b * nc * H + h) * pne + q) * E;  // chunk 0's first element
+    const int64_t stride = (int64_t)H * pne * E;              // one chunk further
+    const T *st = reinterpret_cast<const T *>(p.states) + first;
+    T *prev = reinterpret_cast<T *>(p.prev) + first;
     int cj = -2;  // chunk whose entering state the state-at-index step reads
     if (p.hj && p.state_out_idx) {
         const int j = p.state_out_idx[b];
         cj = j < 0 ? -1 : (int)(min((int64_t)j, p.seqlen - 1) / Q);
     }
+    float *hj = p.hj ? p.hj + e * E : nullptr;
     // Nothing accepted: the state-at-index step copies the initial state
     // from hj (init_state itself may be overwritten by final_state).
-    if (cj == -1) reinterpret_cast<f32x4 *>(p.hj)[e] = hc;
+    if (cj == -1) store_f32<E>(hj, hc);
 
-#pragma unroll 1
-    for (int c0 = 0; c0 < nc; c0 += kBatchChunks) {
-        f32x4 s[kBatchChunks];
-        float a[kBatchChunks];
+    typedef typename Raw16<T>::type RawT;
+    RawT s0[kBatchChunks], s1[kBatchChunks];
+    float a0[kBatchChunks], a1[kBatchChunks];
+    auto load_batch = [&](int c0, RawT (&s)[kBatchChunks], float (&a)[kBatchChunks]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             if (c0 + k < nc) {
-                s[k] = load4<T>(st + 4 * (c0 + k) * stride);
+                s[k] = *reinterpret_cast<const RawT *>(st + (int64_t)(c0 + k) * stride);
                 a[k] = exp_neg(cs_last[(int64_t)(c0 + k) * Q]);
             }
         }
+    };
+    auto combine = [&](int c0, const RawT (&s)[kBatchChunks], const float (&a)[kBatchChunks]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             const int c = c0 + k;
             if (c < nc) {
-                if (c > 0 || p.init_state) store4<T>(prev + 4 * c * stride, hc);
-                if (c == cj) reinterpret_cast<f32x4 *>(p.hj)[e] = hc;
-                hc = a[k] * hc + s[k];
+                if (c > 0 || p.init_state) store_lane<T, E>(prev + (int64_t)c * stride, hc);
+                if (c == cj) store_f32<E>(hj, hc);
+                const LaneT sk = widen<T, E>(s[k]);
+#pragma unroll
+                for (int i = 0; i < E / 4; ++i) hc.v[i] = a[k] * hc.v[i] + sk.v[i];
             }
         }
+    };
+    load_batch(0, s0, a0);
+#pragma unroll 1
+    for (int c0 = 0; c0 < nc; c0 += 2 * kBatchChunks) {
+        if (c0 + kBatchChunks < nc) load_batch(c0 + kBatchChunks, s1, a1);
+        combine(c0, s0, a0);
+        if (c0 + kBatchChunks >= nc) break;
+        if (c0 + 2 * kBatchChunks < nc) load_batch(c0 + 2 * kBatchChunks, s0, a0);
+        combine(c0 + kBatchChunks, s1, a1);
     }
-    if (p.final_state) reinterpret_cast<f32x4 *>(p.final_state)[e] = hc;
+    if (p.final_state) store_f32<E>(p.final_state + e * E, hc);
 }
 
 // seqlen == 0: the final state (and a state_out at index -1) is the initial state.
@@ -120,8 +148,9 @@ __global__ __launch_bounds__(256) void empty_sequence_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_state_pass(const Params &p, Elem e, hipStream_t stream) {
-    const int64_t n4 = p.batch * p.nheads * (int64_t)p.headdim * p.dstate / 4;
-    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    // (headdim * dstate is a multiple of 256: every lane has whole 16 bytes.)
+    const int64_t lanes = p.batch * p.nheads * (int64_t)p.headdim * p.dstate / (e == Elem::BF16 ? 8 : 4);
+    const unsigned blocks = (unsigned)((lanes + 255) / 256);
     if (e == Elem::BF16)
         hipLaunchKernelGGL(state_pass_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, p);
     else

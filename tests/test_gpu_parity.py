@@ -420,6 +420,7 @@ N256 = [
     (1, 2500, 64, 64, 256, 1, 256, True, True),    # 64 items, 10 chunks, last partial
     (2, 1300, 16, 64, 256, 2, 128, False, True),   # 32 items, zero start
     (1, 777, 8, 128, 256, 1, 256, True, False),    # headdim 128, 8 heads
+    (2, 2000, 64, 64, 256, 1, 256, True, True),    # 128 items, 8 chunks: head-batched chunk states, n in halves
 ]
 
 
