@@ -89,8 +89,8 @@ def step_bytes(wl):
 def kernel_bytes(wl):
     """Minimal HBM bytes of each chunk-parallel kernel on its own: the
     tensors it must read or write once, including the workspace
-    intermediates it exchanges with the other kernels (cs, ct, dte and the
-    chunk states in fp32, the states entering each chunk in the input
+    intermediates it exchanges with the other kernels (cs, ct, dte in fp32,
+    the chunk states and the states entering each chunk in the input
     dtype).  The single pass and one_chunk exchange nothing: their bytes are
     the step's."""
     b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
@@ -99,7 +99,7 @@ def kernel_bytes(wl):
     x, bc, dt = b * T * H * P * e, b * T * G * N * e, b * T * H * 4
     tab = b * H * nc * wl.chunk * 4
     st = b * H * P * N * 4
-    S = nc * st
+    S = nc * st // 4 * e
     prev = (nc if wl.init_state else nc - 1) * st // 4 * e
     out = {"chunk_cumsum": dt + 3 * tab,
            "chunk_state": x + bc + dt + tab + S,
