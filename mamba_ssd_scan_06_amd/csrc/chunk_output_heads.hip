@@ -17,6 +17,13 @@
 // G^T[j][i] = B_j . C_i once into registers (phase A), and then runs over its
 // heads, each head only scaling G^T and multiplying by x (phase B).
 //
+// Channels.  The rows p of the state are independent, so a workgroup may
+// own P of a head's channels (x, y and the state rows of that slice); the
+// head's G^T is then formed once per channel slice.  dstate 256 with
+// 256-token chunks runs 32-channel slices in the one-tile-per-wave layout:
+// two buffers of a 32-channel head fit in LDS next to the B ring, and 16
+// waves share the compute unit instead of the 8 of the two-tile layout.
+//
 // Work split.  The chunk's 16-token column tiles ("i-tiles") are dealt to
 // W = tiles/2 waves, wave w owning tiles w and tiles-1-w, so every wave holds
 // the same number of causal (i-tile, 32-token j block) pairs.  Tile t meets
@@ -104,7 +111,8 @@ struct HeadsCfg {
 
 template <int NT, int PT, int NIT, bool WIDE>
 __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) void chunk_output_heads_kernel(Params p, int hps,
-                                                                                                  int nslices) {
+                                                                                                  int nslices,
+                                                                                                  int csplit) {
     using Cf = HeadsCfg<NT, PT, NIT, WIDE>;
     using T = bf16;
     constexpr int N = Cf::N, P = Cf::P, KS = Cf::KS, NP = Cf::NP, WB = Cf::WB, WX = Cf::WX, W = Cf::W;
@@ -147,12 +155,18 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
 
     const int Q = p.chunk, H = p.nheads, G = p.ngroups, nc = p.nchunks, HPG = p.heads_per_group;
     const int64_t L = p.seqlen;
+    // Channels: a workgroup owns P of the head's PF = csplit P channels
+    // (rows p of the state are independent), channel slice cs.
+    const int PF = P * csplit;
 
-    // Workgroup -> (b, c, g, slice); slices of one (b, c) run back to back on one XCD.
-    const int64_t total = p.batch * nc * G * nslices;
+    // Workgroup -> (b, c, g, slice, channel slice); the slices of one (b, c)
+    // run back to back on one XCD.
+    const int64_t total = p.batch * nc * G * nslices * csplit;
     const int64_t per_xcd = gridDim.x / kXcds;
-    const int64_t logical = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (logical >= total) return;
+    const int64_t logical0 = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical0 >= total) return;
+    const int cs = (int)(logical0 % csplit);
+    const int64_t logical = logical0 / csplit;
     const int slice = (int)(logical % nslices);
     const int g = (int)((logical / nslices) % G);
     const int c = (int)((logical / ((int64_t)nslices * G)) % nc);
@@ -217,7 +231,7 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
     for (int u = 0; u < Cf::UX; ++u) {
         const int U = 64 * (wave + W * u) + lane;
         const int row = U / WX, pos = U - row * WX;
-        offx[u] = (uint32_t)min(row, Qc - 1) * (uint32_t)(H * P) + 8 * (pos ^ xsw<WX>(row));
+        offx[u] = (uint32_t)min(row, Qc - 1) * (uint32_t)(H * PF) + 8 * (pos ^ xsw<WX>(row));
     }
 #pragma unroll
     for (int u = 0; u < Cf::UH; ++u) {
@@ -244,7 +258,7 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
             oh[u] = offh[u];
             asm volatile("" : "+v"(oh[u]));
         }
-        const T *xsrc = xg + ((b * L + t0) * H + h) * P;
+        const T *xsrc = xg + ((b * L + t0) * H + h) * PF + cs * P;
         T *xdst = xbuf(bc);
 #pragma unroll
         for (int u = 0; u < Cf::UX; ++u) {
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
             else copy16_to_lds(xsrc, junk);
         }
         if (has_prev) {
-            const T *hsrc = hg + (((b * nc + c) * H + h) * (int64_t)P) * N;
+            const T *hsrc = hg + (((b * nc + c) * H + h) * (int64_t)PF + cs * P) * N;
             T *hdst = hbuf(bc);
 #pragma unroll
             for (int u = 0; u < Cf::UH; ++u) {
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
     // Per-lane output offsets within one head's rows: token i, channels 16q + 4grp.
     uint32_t yoff[MAXIT];
 #pragma unroll
-    for (int k = 0; k < MAXIT; ++k) yoff[k] = (uint32_t)(16 * tile[k] + il) * (uint32_t)(H * P) + 4 * grp;
+    for (int k = 0; k < MAXIT; ++k) yoff[k] = (uint32_t)(16 * tile[k] + il) * (uint32_t)(H * PF) + 4 * grp;
 
     auto head = [&](auto bc, int hh) __attribute__((always_inline)) {
         constexpr int BI = decltype(bc)::value;
@@ -591,7 +605,7 @@ __global__ __launch_bounds__(WIDE ? 64 * NIT : 64 * (NIT >= 2 ? NIT / 2 : 1)) vo
         // D through the constant address space: a scalar load, which vmcnt
         // does not count (a vector load here would have to wait for the copies).
         const float dh = p.D ? ((const __attribute__((address_space(4))) float *)(uintptr_t)p.D)[h] : 0.f;
-        T *yh = yg + ((b * L + t0) * H + h) * P;
+        T *yh = yg + ((b * L + t0) * H + h) * PF + cs * P;
         // Head hh+1's copies have landed: its loads precede the last head's
         // in issue order and loads complete in order (pending older stores
         // only make the wait stricter).
@@ -641,14 +655,15 @@ hipError_t launch_nit(const Params &p, hipStream_t stream) {
     if constexpr (Cf::LDS_BYTES > 160 * 1024) {
         return hipErrorNotSupported;
     } else {
-        const int64_t base = p.batch * p.nchunks * (int64_t)p.ngroups;
+        const int csplit = p.headdim / Cf::P;  // channel slices per head
+        const int64_t base = p.batch * p.nchunks * (int64_t)p.ngroups * csplit;
         int nslices = (int)std::min<int64_t>(p.heads_per_group, std::max<int64_t>(1, (256 + base - 1) / base));
         const int hps = (p.heads_per_group + nslices - 1) / nslices;
         nslices = (p.heads_per_group + hps - 1) / hps;
         const int64_t total = base * nslices;
         const int64_t per_xcd = (total + kXcds - 1) / kXcds;
         hipLaunchKernelGGL((chunk_output_heads_kernel<NT, PT, NIT, WIDE>), dim3((unsigned)(per_xcd * kXcds)),
-                           dim3(Cf::THREADS), 0, stream, p, hps, nslices);
+                           dim3(Cf::THREADS), 0, stream, p, hps, nslices, csplit);
         return hipGetLastError();
     }
 }
@@ -656,6 +671,12 @@ hipError_t launch_nit(const Params &p, hipStream_t stream) {
 // Shapes whose one-tile-per-wave variant fits 128 VGPRs.
 template <int NT, int PT>
 constexpr bool kWideOk = NT <= 8 && PT <= 4;
+// dstate 256 with 256-token chunks runs 32-channel workgroups in the
+// one-tile-per-wave layout (a head's buffers then fit LDS next to the B ring,
+// and 16 waves share a compute unit instead of 8).
+#ifndef SSD_OUT_SPLIT256
+#define SSD_OUT_SPLIT256 1
+#endif
 
 template <int NT, int PT>
 hipError_t dispatch_q(const Params &p, hipStream_t stream) {
@@ -665,7 +686,9 @@ hipError_t dispatch_q(const Params &p, hipStream_t stream) {
         case 32: return launch_nit<NT, PT, 2, false>(p, stream);
         case 64: return launch_nit<NT, PT, 4, false>(p, stream);
         case 128: return launch_nit<NT, PT, 8, kWideOk<NT, PT>>(p, stream);
-        case 256: return launch_nit<NT, PT, 16, kWideOk<NT, PT>>(p, stream);
+        case 256:
+            if constexpr (SSD_OUT_SPLIT256 && NT == 16 && PT >= 2) return launch_nit<NT, 2, 16, true>(p, stream);
+            else return launch_nit<NT, PT, 16, kWideOk<NT, PT>>(p, stream);
         default: return hipErrorNotSupported;
     }
 }
