@@ -120,10 +120,16 @@ def total_flops(wl):
 
 
 def source_hash(kernel):
+    """Hash of a kernel's sources and of the compiler flags they are built
+    with (absolute include paths left out, so the hash is the same in every
+    checkout)."""
+    from mamba_ssd_scan_06_amd import build as _build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(kernel, []):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
+        flags = [a for a in _build.HIPCC_FLAGS + _build.EXTRA_FLAGS.get(f, []) if not os.path.isabs(a)]
+        h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

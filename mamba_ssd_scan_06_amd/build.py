@@ -30,6 +30,17 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags on top of HIPCC_FLAGS.  The iterative ILP machine
+# scheduler interleaves more of each block's independent products, reads
+# and scaling in the kernels below (same instructions, so bitwise-identical
+# results); measured on MI355X it shortens the single pass by 3-5% and the
+# head-batched chunk states by about 15%, and slows the output kernel.
+EXTRA_FLAGS = {
+    "chunk_scan_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "chunk_state_heads.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -47,7 +58,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
