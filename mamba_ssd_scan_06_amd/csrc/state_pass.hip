@@ -23,7 +23,10 @@
 // E = 8 for bf16 chunk states, 4 for fp32), sequential over chunks.  The
 // chunk states are loaded in batches of kBatchChunks chunks, and the loads of
 // the next batch are issued before the current one is combined, so that two
-// batches of loads per lane are in flight.
+// batches of loads per lane are in flight.  The chunk states are read for
+// the last time here: non-temporal loads, so that the entering states this
+// kernel writes, which the output kernel reads next, take their place in the
+// last-level cache.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(Params p) {
 #pragma unroll
         for (int k = 0; k < kBatchChunks; ++k) {
             if (c0 + k < nc) {
-                s[k] = *reinterpret_cast<const RawT *>(st + (int64_t)(c0 + k) * stride);
+                s[k] = __builtin_nontemporal_load(reinterpret_cast<const RawT *>(st + (int64_t)(c0 + k) * stride));
                 a[k] = exp_neg(cs_last[(int64_t)(c0 + k) * Q]);
             }
         }
