@@ -64,7 +64,13 @@ KERNEL_SOURCES = {
     "chunk_scan_fused": ["chunk_scan_fused.hip", "device_common.hpp"],
     "one_chunk": ["one_chunk.hip", "device_common.hpp"],
     "empty_sequence": ["state_pass.hip"],
+    "state_correction": ["state_correction.hip", "device_common.hpp"],
 }
+# One GPU's shard of the 16K-token dstate-256 workload on 8 GPUs (2048 tokens),
+# corrected in place once the state entering it is known (sequence sharding).
+CP_SHARD = ssd_inputs.Workload("long_16k_n256_shard", 1, 2048, 64, 64, 256, 1, 256, "bf16", init_state=True,
+                               seed=1102)
+ALL_WORKLOADS = {**ssd_inputs.WORKLOADS, CP_SHARD.name: CP_SHARD}
 CSRC = os.path.join(ROOT, "mamba_ssd_scan_06_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -86,6 +92,15 @@ def step_bytes(wl):
             + (st if wl.init_state else 0) + (st + 4 * b if wl.state_out else 0))
 
 
+def correction_bytes(wl):
+    """Minimal HBM bytes of ssd_state_correction on a shard: y read and
+    written, C, dt and A read, h_in and the shard's final state read, the
+    corrected final state written."""
+    b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    e = 2 if wl.dtype == "bf16" else 4
+    return 2 * b * T * H * P * e + b * T * G * N * e + b * T * H * 4 + H * 4 + 3 * b * H * P * N * 4
+
+
 def kernel_bytes(wl):
     """Minimal HBM bytes of each chunk-parallel kernel on its own: the
     tensors it must read or write once, including the workspace
@@ -105,7 +120,8 @@ def kernel_bytes(wl):
            "chunk_state": x + bc + dt + tab + S,
            "state_pass": S + prev + st + (st if wl.init_state else 0),
            "chunk_output": 2 * x + 2 * bc + 3 * tab + prev,
-           "chunk_scan_fused": step_bytes(wl), "one_chunk": step_bytes(wl)}
+           "chunk_scan_fused": step_bytes(wl), "one_chunk": step_bytes(wl),
+           "state_correction": correction_bytes(wl)}
     return out
 
 
@@ -304,6 +320,60 @@ def time_decode(steps, warmup, device):
             "state_GB/s": round(state_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def time_state_correction(steps, warmup, device):
+    """ssd_state_correction on a sequence shard, back to back on the same
+    buffers (each call adds the correction again: the values change, the
+    work does not), next to the shard's own forward from a zero state."""
+    import torch
+
+    import mamba_ssd_scan_06_amd as ssd
+
+    wl = CP_SHARD
+    inp = ssd_inputs.generate(wl)
+    dev = device_inputs(inp, device)
+    b, T, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    y, fin, _ = ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], None, wl.chunk)
+    h_in = dev["init_state"]
+    out = torch.empty_like(fin)
+
+    # The binding checks every tensor on each call, which takes longer than
+    # the kernel: the timed loop calls the C entry point with its arguments
+    # marshalled once (the first call goes through the binding's checks).
+    ssd.ssd_state_correction(y, dev["dt"], dev["A"], dev["C"], h_in, shard_final=fin, final_state=out)
+    lib = ssd._load()
+    shape = ssd.make_shape(b, T, H, P, N, G)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    cargs = (ssd._ptr(y), ssd._ptr(dev["dt"]), ssd._ptr(dev["A"]), ssd._ptr(dev["C"]), ssd._ptr(h_in),
+             ssd._ptr(fin), ssd._ptr(out), None, None, ctypes.byref(shape), ssd.SSD_DTYPE_BF16, stream)
+
+    def corr():
+        if lib.ssd_state_correction(*cargs) != 0:
+            raise RuntimeError(ssd.ssd_last_error())
+
+    def fwd():
+        ssd.ssd_chunk_scan_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], None, wl.chunk,
+                               y=y, final_state=fin)
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us = timed(corr)
+    fwd_us = timed(fwd)
+    nbytes = correction_bytes(wl)
+    return {"workload": wl.name, "batch": b, "seqlen": T, "nheads": H, "headdim": P, "dstate": N,
+            "us_per_call": round(us, 2), "alg_bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+            "shard_forward_us": round(fwd_us, 2)}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -399,7 +469,7 @@ def summarize_stats(d, workload=HEADLINE, command="", steps=None, warmup=None, c
 
 
 KERNEL_KEYS = ("chunk_scan_fused", "one_chunk", "chunk_output", "chunk_state", "state_pass", "chunk_cumsum",
-               "empty_sequence")
+               "empty_sequence", "state_correction")
 # fp32 inputs run v_mfma_f32_16x16x4_f32 (2048 flops), bf16 v_mfma_f32_16x16x32_bf16 (16384).
 MFMA_FLOPS = {"bf16": 16384, "f32": 2048}
 N_SIMDS, N_SE = 1024, 32
@@ -436,7 +506,7 @@ def summarize_pmc(dirs, workload=HEADLINE, commands=()):
         vals = sorted(per.get(key, {}).get(counter, {}).values())
         return vals[len(vals) // 2] if vals else None
 
-    wl = ssd_inputs.WORKLOADS[workload]
+    wl = ALL_WORKLOADS[workload]
     copy_bytes = 256 << 20
     # The copy probe runs last: its three 256 MiB copies are the last three
     # copy dispatches of each run (earlier ones upload the inputs).
@@ -504,7 +574,9 @@ def main():
     # ~0.2 s of untimed steps: the GPU's clocks ramp up over the first milliseconds.
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--cold-steps", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=list(ssd_inputs.WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=list(ALL_WORKLOADS))
+    ap.add_argument("--state-correction-only", action="store_true",
+                    help="time ssd_state_correction on a sequence shard and print its figures")
     ap.add_argument("--path", default="auto", choices=["auto", "one_chunk", "single_pass", "chunk_parallel"])
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads and the decode line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -531,6 +603,11 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
 
+    if args.state_correction_only:
+        print(json.dumps(time_state_correction(args.steps, args.warmup, device)), flush=True)
+        if args.copy_probe:
+            copy_probe(device)
+        return
     wl = ssd_inputs.WORKLOADS[args.workload]
     inp, res = time_workload(wl, args.steps, args.warmup, device, args.path, args.cold_steps)
     ms = res["ms_per_step"]
@@ -553,6 +630,7 @@ def main():
                                "warm": r2["warm"], "cold": r2["cold"]}
 
     decode = None if args.headline_only else time_decode(max(20, args.steps // 2), 5, device)
+    correction = None if args.headline_only else time_state_correction(max(20, args.steps // 2), 20, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, inp)
     line = {
         "metric": METRIC,
@@ -583,6 +661,7 @@ def main():
         "kernels": res["kernels"],
         "workloads": workloads,
         "decode": decode,
+        "state_correction": correction,
         "input_sha256": inp.sha256,
     }
     if args.copy_probe:

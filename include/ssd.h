@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 
 /* Element type of x, B, C and y.  dt, A, D and every state are always fp32. */
 typedef enum {
@@ -261,6 +261,43 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
                                       void *y, float *final_state,
                                       const int32_t *state_out_idx, float *state_out,
                                       const ssd_shape *shape, ssd_dtype dtype, void *hip_stream);
+
+/* Sequence sharding (context parallelism): the step a GPU runs on its shard
+ * once it knows the state entering the shard.
+ *
+ * "Transformers are SSMs" article (cloud.tencent.com.cn), section
+ * "序列并行的两种形式": with the sequence split over GPUs, each GPU computes
+ * its shard's outputs and final state on its own and only states pass between
+ * GPUs.  A shard run with ssd_chunk_scan_fwd from a zero initial state gives
+ * y0, F (its final_state) and, with an accepted index, h0_j (its state_out).
+ * The recurrence is linear in its initial state, so from the true entering
+ * state h_in the shard's results are
+ *     y_t   = y0_t + exp(cs_t) * sum_n C[b,t,g,n] * h_in[b,h,p,n]
+ *     final = F + exp(cs_{T-1}) * h_in
+ *     h_j   = h0_j + exp(cs_j) * h_in          (j = -1: h0_j + h_in)
+ * with cs_t = A[h] * sum_{k<=t} dt[b,k,h] over the shard's own tokens.  This
+ * call applies them in place; the exchange of states between GPUs is the
+ * caller's.
+ *
+ *   y             [b,T,H,P]  dtype  in/out: y0 on entry, y on return (rounded
+ *                                   to nearest even from fp32 for bf16)
+ *   dt, A, C      as passed to ssd_chunk_scan_fwd for the shard
+ *   h_in          [b,H,P,N]  fp32   state entering the shard (required)
+ *   shard_final   [b,H,P,N]  fp32   F; required when final_state is given
+ *   final_state   [b,H,P,N]  fp32   out: F + exp(cs_{T-1}) h_in; NULL = not
+ *                                   returned; may be shard_final itself
+ *   state_out_idx [b]        int32  the accepted index j_b within the shard
+ *                                   (as given to the shard's forward); NULL = none
+ *   state_out     [b,H,P,N]  fp32   in/out: h0_j on entry, h_j on return;
+ *                                   non-NULL exactly when state_out_idx is
+ * h_in rounds once to dtype before its product with C (fp32 accumulation).
+ * Outputs must not overlap the inputs or each other (final_state ==
+ * shard_final excepted).  Same shape limits, alignment rules and errors as
+ * ssd_chunk_scan_fwd; no workspace; T = 0 gives final = F + h_in. */
+ssd_status ssd_state_correction(void *y, const float *dt, const float *A, const void *C,
+                                const float *h_in, const float *shard_final, float *final_state,
+                                const int32_t *state_out_idx, float *state_out,
+                                const ssd_shape *shape, ssd_dtype dtype, void *hip_stream);
 
 /* Static description of a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "SsdError", "ssd_abi_version", "ssd_status_string", "ssd_last_error", "ssd_workspace_bytes",
     "ssd_get_workspace_layout", "ssd_select_path", "ssd_chunk_scan_fwd", "ssd_chunk_scan_fwd_ex",
-    "ssd_chunk_scan_fwd_noalloc", "SSD_NOALLOC_SCRATCH_BYTES", "workspace_views", "library_path", "SSD_PATH_AUTO", "SSD_PATH_ONE_CHUNK", "SSD_PATH_SINGLE_PASS",
+    "ssd_chunk_scan_fwd_noalloc", "ssd_state_correction", "SSD_NOALLOC_SCRATCH_BYTES", "workspace_views", "library_path", "SSD_PATH_AUTO", "SSD_PATH_ONE_CHUNK", "SSD_PATH_SINGLE_PASS",
     "SSD_PATH_CHUNK_PARALLEL",
 ]
 
@@ -88,6 +88,8 @@ def _load():
     lib.ssd_chunk_scan_fwd_ex.restype = i32
     lib.ssd_chunk_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, shp, i32, vp]
     lib.ssd_chunk_scan_fwd_noalloc.restype = i32
+    lib.ssd_state_correction.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, i32, vp]
+    lib.ssd_state_correction.restype = i32
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -188,6 +190,50 @@ def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, init_state=None, chunk_si
     y, final_state, state_out, _ = _run(x, dt, A, B, C, D, init_state, chunk_size, state_out_idx, y, final_state,
                                         return_final_state, state_out, None, stream, SSD_PATH_AUTO, None,
                                         noalloc=True)
+    return y, final_state, state_out
+
+
+def ssd_state_correction(y, dt, A, C, h_in, shard_final=None, final_state=None, state_out_idx=None,
+                         state_out=None, *, stream=None):
+    """Sequence-shard correction in place (see ssd_state_correction in
+    include/ssd.h): y [b,T,H,P] holds the shard's outputs from a zero initial
+    state and becomes those from h_in [b,H,P,N]; final_state (may be
+    shard_final itself) receives shard_final + exp(cs_{T-1}) h_in; state_out,
+    given with state_out_idx, gains exp(cs_j) h_in.  dt, A, C as for the
+    shard's forward.  Returns (y, final_state, state_out)."""
+    import torch
+
+    if y.dim() != 4 or C.dim() != 4:
+        raise ValueError("y must be [b,T,H,P] and C [b,T,G,N]")
+    b, T, H, P = y.shape
+    G, N = C.shape[2], C.shape[3]
+    code = _dtype_code(torch, y)
+    dev = y.device
+    state_shape = (b, H, P, N)
+    _expect("y", y, y.shape, y.dtype, dev)
+    _expect("C", C, (b, T, G, N), y.dtype, dev)
+    _expect("dt", dt, (b, T, H), torch.float32, dev)
+    _expect("A", A, (H,), torch.float32, dev)
+    _expect("h_in", h_in, state_shape, torch.float32, dev)
+    if shard_final is not None:
+        _expect("shard_final", shard_final, state_shape, torch.float32, dev)
+    if final_state is not None:
+        _expect("final_state", final_state, state_shape, torch.float32, dev)
+    if state_out_idx is not None:
+        _expect("state_out_idx", state_out_idx, (b,), torch.int32, dev)
+    if state_out is not None:
+        _expect("state_out", state_out, state_shape, torch.float32, dev)
+    if (state_out is None) != (state_out_idx is None):
+        raise ValueError("state_out and state_out_idx go together")
+    if not y.is_cuda:
+        raise ValueError(f"tensors must be on a GPU device, y is on {dev}")
+    lib = _load()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.ssd_state_correction(_ptr(y), _ptr(dt), _ptr(A), _ptr(C), _ptr(h_in), _ptr(shard_final),
+                                    _ptr(final_state), _ptr(state_out_idx), _ptr(state_out),
+                                    ctypes.byref(make_shape(b, T, H, P, N, G)), code,
+                                    ctypes.c_void_p(stream) if stream else None))
     return y, final_state, state_out
 
 

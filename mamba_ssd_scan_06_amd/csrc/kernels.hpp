@@ -31,6 +31,7 @@ struct Params {
                               // rounded once to the input type
     void *prev;               // workspace [b,nc,H,P,N] T_elem: state entering each chunk (chunk 0 only with init_state)
     float *hj;                // workspace [b,H,P,N] fp32: state entering the chunk of state_out_idx[b]
+    const float *shard_final; // [b,H,P,N] fp32: a shard's final state from a zero start (state correction only)
     int64_t batch, seqlen;
     int nheads, headdim, dstate, ngroups, chunk, nchunks;
     int heads_per_group;
@@ -67,5 +68,11 @@ hipError_t launch_chunk_scan_fused(const Params &p, hipStream_t stream);
 bool one_chunk_takes(const Params &p);
 hipError_t launch_one_chunk(const Params &p, Elem e, hipStream_t stream);
 hipError_t launch_empty_sequence(const Params &p, hipStream_t stream);
+// Sequence-shard correction: y += exp(cs_t) C_t . init_state over the whole
+// shard (cs from the shard's first token), final_state = shard_final +
+// exp(cs_{T-1}) init_state, state_out += exp(cs_j) init_state.  Reads
+// init_state (the state entering the shard), dt, A, C, shard_final and
+// state_out_idx; updates y and state_out in place.
+hipError_t launch_state_correction(const Params &p, Elem e, hipStream_t stream);
 
 }  // namespace ssd

@@ -409,6 +409,73 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
                               shape, dtype, ws, need > 0 ? (size_t)SSD_NOALLOC_SCRATCH_BYTES : 0, hip_stream);
 }
 
+ssd_status ssd_state_correction(void *y, const float *dt, const float *A, const void *C, const float *h_in,
+                                const float *shard_final, float *final_state, const int32_t *state_out_idx,
+                                float *state_out, const ssd_shape *shape, ssd_dtype dtype, void *hip_stream) {
+    ssd_status st = check_shape(shape, 256, dtype);
+    if (st != SSD_OK) return st;
+    const int64_t b = shape->batch, T = shape->seqlen, H = shape->nheads, P = shape->headdim, N = shape->dstate,
+                  G = shape->ngroups;
+    if ((state_out == nullptr) != (state_out_idx == nullptr))
+        return fail(SSD_ERR_ARGS, "state_out and state_out_idx must be given together");
+    if (final_state && !shard_final) return fail(SSD_ERR_NULL, "final_state needs shard_final");
+    if (b > 0 && !h_in) return fail(SSD_ERR_NULL, "h_in is required");
+    if (b > 0 && T > 0 && (!y || !dt || !A || !C)) return fail(SSD_ERR_NULL, "y, dt, A and C are required");
+    // The kernel addresses a 64-token block's rows of y and C, and a
+    // sequence's dt, with 32-bit byte offsets.
+    const int64_t esz_i = dtype == SSD_DTYPE_BF16 ? 2 : 4, lim31 = (int64_t)1 << 31;
+    if (64 * H * P * esz_i >= lim31 || 64 * G * N * esz_i >= lim31 || T * H * 4 >= lim31)
+        return fail(SSD_ERR_UNSUPPORTED, "state correction needs 64*nheads*headdim, 64*ngroups*dstate "
+                                         "(in elements of dtype) and seqlen*nheads*4 below 2^31 bytes");
+
+    const size_t esz = dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const size_t n_tok = (size_t)b * T;
+    const size_t y_bytes = n_tok * H * P * esz, c_bytes = n_tok * G * N * esz;
+    const size_t dt_bytes = n_tok * H * sizeof(float), state_bytes = (size_t)b * H * P * N * sizeof(float);
+    const void *aligned16[] = {y, C, h_in, shard_final, final_state, state_out};
+    const char *names16[] = {"y", "C", "h_in", "shard_final", "final_state", "state_out"};
+    for (int k = 0; k < 6; ++k)
+        if ((uintptr_t)aligned16[k] % 16 != 0) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", names16[k]);
+    const void *aligned4[] = {dt, A, state_out_idx};
+    const char *names4[] = {"dt", "A", "state_out_idx"};
+    for (int k = 0; k < 3; ++k)
+        if ((uintptr_t)aligned4[k] % 4 != 0) return fail(SSD_ERR_ALIGN, "%s is not 4-byte aligned", names4[k]);
+
+    const Range outs[] = {range("y", y, y_bytes), range("final_state", final_state, state_bytes),
+                          range("state_out", state_out, state_bytes)};
+    const Range others[] = {range("dt", dt, dt_bytes), range("A", A, H * sizeof(float)), range("C", C, c_bytes),
+                            range("h_in", h_in, state_bytes), range("shard_final", shard_final, state_bytes),
+                            range("state_out_idx", state_out_idx, b * sizeof(int32_t))};
+    // final_state may be shard_final itself: each element is read before it
+    // is written, by the same thread, and read nowhere else.
+    const bool in_place = final_state != nullptr && (const void *)final_state == (const void *)shard_final;
+    for (int i = 0; i < 3; ++i) {
+        for (const Range &o : others) {
+            if (in_place && i == 1 && o.lo == (uintptr_t)shard_final) continue;
+            if (overlaps(outs[i], o)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, o.name);
+        }
+        for (int k = i + 1; k < 3; ++k)
+            if (overlaps(outs[i], outs[k])) return fail(SSD_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[k].name);
+    }
+    if (b == 0 || (T == 0 && !final_state && !state_out)) return SSD_OK;  // nothing to enqueue
+
+    ssd::Params p = shape_params(shape, 256);
+    p.dt = dt;
+    p.A = A;
+    p.C = C;
+    p.init_state = h_in;
+    p.shard_final = shard_final;
+    p.state_out_idx = state_out_idx;
+    p.y = y;
+    p.final_state = final_state;
+    p.state_out = state_out;
+    (void)hipGetLastError();  // start from a clean error state
+    const hipError_t r = ssd::launch_state_correction(
+        p, dtype == SSD_DTYPE_BF16 ? ssd::Elem::BF16 : ssd::Elem::F32, static_cast<hipStream_t>(hip_stream));
+    if (r != hipSuccess) return fail(SSD_ERR_HIP, "state_correction launch failed: %s", hipGetErrorString(r));
+    return SSD_OK;
+}
+
 const char *ssd_status_string(ssd_status s) {
     switch (s) {
         case SSD_OK: return "ok";

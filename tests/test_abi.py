@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert ssd.ssd_abi_version() == 7
+    assert ssd.ssd_abi_version() == 8
 
 
 def test_status_strings():
@@ -310,3 +310,59 @@ def test_binding_rejects_bad_x():
         _call(dict(kw, x=kw["x"].half()))
     with pytest.raises(ValueError):
         _call(dict(kw, x=kw["x"][0]))
+
+
+class CorrArgs:
+    """ssd_state_correction arguments at fake, never-dereferenced addresses."""
+
+    def __init__(self, s, dtype=ssd.SSD_DTYPE_BF16):
+        self.s, self.dtype = s, dtype
+        self.p = {k: BASE + i * 256 * MB for i, k in enumerate(
+            ["y", "dt", "A", "C", "h_in", "shard_final", "final", "idx", "sout"])}
+
+    def call(self):
+        v = lambda k: None if self.p[k] is None else ctypes.c_void_p(self.p[k])
+        return ssd._load().ssd_state_correction(v("y"), v("dt"), v("A"), v("C"), v("h_in"), v("shard_final"),
+                                                 v("final"), v("idx"), v("sout"), ctypes.byref(self.s),
+                                                 self.dtype, None)
+
+
+@pytest.mark.parametrize("key", ["y", "dt", "A", "C", "h_in"])
+def test_correction_null_required(key):
+    a = CorrArgs(shape())
+    a.p[key] = None
+    assert a.call() == ERR_NULL
+
+
+def test_correction_argument_errors():
+    a = CorrArgs(shape())
+    a.p["shard_final"] = None                 # final_state without the shard's own final state
+    assert a.call() == ERR_NULL
+    a = CorrArgs(shape())
+    a.p["idx"] = None                         # state_out without its index
+    assert a.call() == ERR_ARGS
+    a = CorrArgs(shape())
+    a.p["h_in"] += 8                          # misaligned state
+    assert a.call() == ERR_ALIGN
+    a = CorrArgs(shape())
+    a.p["final"] = a.p["h_in"]                # the result may not overwrite h_in
+    assert a.call() == ERR_ALIAS
+    a = CorrArgs(shape())
+    a.p["sout"] = a.p["y"] + 64               # outputs may not overlap
+    assert a.call() == ERR_ALIAS
+    assert CorrArgs(shape(H=4, G=3)).call() == ERR_SHAPE
+    assert CorrArgs(shape(P=48)).call() == ERR_UNSUPPORTED
+
+
+def test_correction_binding_refuses_mis_sized_tensors():
+    import torch
+    y = torch.zeros(1, 8, 2, 16, dtype=torch.bfloat16)
+    C = torch.zeros(1, 8, 1, 16, dtype=torch.bfloat16)
+    dt = torch.zeros(1, 8, 2)
+    A = torch.zeros(2)
+    with pytest.raises(ValueError):
+        ssd.ssd_state_correction(y, dt, A, C, torch.zeros(1, 2, 16, 8))          # h_in of the wrong shape
+    with pytest.raises(TypeError):
+        ssd.ssd_state_correction(y, dt, A, C.float(), torch.zeros(1, 2, 16, 16))  # C of another dtype
+    with pytest.raises(ValueError):
+        ssd.ssd_state_correction(y, dt, A, C, torch.zeros(1, 2, 16, 16))          # CPU tensors

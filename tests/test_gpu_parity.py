@@ -27,7 +27,7 @@ def check(name, got, ref, tol):
 def library_loaded():
     # No fallback exists: the HIP library must be there on a GPU machine.
     assert torch.cuda.is_available()
-    assert ssd.ssd_abi_version() == 7
+    assert ssd.ssd_abi_version() == 8
 
 
 # ----------------------------------------------------------- full workloads
