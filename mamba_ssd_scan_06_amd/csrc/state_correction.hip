@@ -17,7 +17,8 @@
 // with the whole shard as one chunk.
 //
 // One workgroup (4 waves) per (b, h, slice of at most 64 channels, range of
-// 64-token blocks), about 256 workgroups in all.  A range not starting at
+// 64-token blocks), about 256 workgroups in all, the ranges of one item on
+// one XCD.  A range not starting at
 // token 0 first sums dt over the tokens before it (fp64); h_in's slice is
 // copied once, rounded to the input type, to LDS.  Per block: wave 0 scans
 // the next block's dt in fp64 and writes its exp(cs_t) per token to LDS
@@ -58,7 +59,12 @@ __global__ __launch_bounds__(kThreads) void state_correction_kernel(Params p, in
     const int nsl = PF / PS;
     const int64_t L = p.seqlen;
     const int nblk = (int)((L + kBlk - 1) / kBlk);
-    const int item = (int)(blockIdx.x / (unsigned)ranges), r = (int)(blockIdx.x % (unsigned)ranges);
+    // Workgroup w runs on XCD w mod 8 (the hardware deals workgroups to the
+    // XCDs in turn): the ranges of one item are given to workgroups of one
+    // XCD, so that they share its L2 copy of the item's h_in slice.
+    const unsigned nwg = gridDim.x, nx = nwg % 8 == 0 ? 8 : 1;
+    const unsigned idx = (blockIdx.x % nx) * (nwg / nx) + blockIdx.x / nx;
+    const int item = (int)(idx / (unsigned)ranges), r = (int)(idx % (unsigned)ranges);
     const int s = item % nsl, bh = item / nsl, h = bh % H;
     const int64_t b = bh / H;
     const int g = h / p.heads_per_group;
