@@ -62,10 +62,26 @@ __global__ __launch_bounds__(64 * kHeads) void chunk_cumsum_kernel(Params p) {
     const int Qc = (int)(L - t0 < Q ? L - t0 : Q);
 
     // dt[b, t0 + i, h0 + k] -> dts[k][i]; consecutive threads read the four
-    // heads of one token, then the next token.
-    for (int e = tid; e < Q * kHeads; e += 64 * kHeads) {
-        const int i = e / kHeads, k = e - i * kHeads;
-        dts[k][i] = (i < Qc && h0 + k < H) ? p.dt[(b * L + t0 + i) * H + h0 + k] : 0.f;
+    // heads of one token, then the next token.  The loads go through a
+    // buffer descriptor over the chunk's dt rows (tokens past the sequence
+    // read as zero), so that they are unconditional and all in flight at
+    // once (a load under a condition gets its own branch and wait).
+    {
+        constexpr int U = 256 * kHeads / (64 * kHeads);  // loads per thread at Q = 256
+        const auto rd = buffer_rsrc(p.dt + (b * L + t0) * H, (uint32_t)((int64_t)Qc * H * 4));
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = tid + u * 64 * kHeads, i = e / kHeads, k = e - i * kHeads;
+            v[u] = e < Q * kHeads ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                  rd, (i * H + h0 + k) * 4, 0, 0))
+                                  : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = tid + u * 64 * kHeads, i = e / kHeads, k = e - i * kHeads;
+            if (e < Q * kHeads) dts[k][i] = h0 + k < H ? v[u] : 0.f;
+        }
     }
     __syncthreads();
     const int h = h0 + wave;
