@@ -135,6 +135,35 @@ def total_flops(wl):
     return b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P + 4 * H * q * N * P for q in qs)
 
 
+def kernel_flops(wl):
+    """Algorithmic flops of each kernel that contracts on the matrix cores
+    (the causal triangle counted once; C.B^T once per chunk and group)."""
+    qs = chunk_lengths(wl)
+    b, H, P, N, G = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    prior = sum(qs[1:]) + (qs[0] if wl.init_state and qs else 0)
+    return {"chunk_state": 2 * b * H * N * P * wl.seqlen,
+            "chunk_output": b * sum(G * q * (q + 1) * N + H * q * (q + 1) * P for q in qs) + 2 * b * H * N * P * prior,
+            "chunk_scan_fused": total_flops(wl), "one_chunk": total_flops(wl),
+            "state_correction": 2 * b * H * N * P * wl.seqlen}
+
+
+def timed_mean_us(key, workload):
+    """A kernel's mean duration in the kernel-trace summary of the same
+    workload (the timed steps where the summary has them, else all calls)."""
+    path = os.path.join(PROFILES, f"kernels_{workload}_kernel_stats.txt")
+    if not os.path.exists(path):
+        return None
+    timed, calls = None, None
+    with open(path) as f:
+        for line in f:
+            parts = [x.strip() for x in line.split("|")]
+            if line.startswith("timed |") and len(parts) >= 4 and _kernel_key(parts[1]) == key:
+                timed = float(parts[3]) / 1e3
+            elif not line.startswith("#") and len(parts) >= 4 and _kernel_key(parts[0]) == key:
+                calls = float(parts[3]) / 1e3
+    return timed if timed is not None else calls
+
+
 def source_hash(kernel):
     """Hash of a kernel's sources and of the compiler flags they are built
     with (absolute include paths left out, so the hash is the same in every
@@ -541,6 +570,21 @@ def summarize_pmc(dirs, workload=HEADLINE, commands=()):
                       f"traffic_bytes_per_launch = {fb + wb:.0f}"]
             if ab:
                 lines += [f"algorithmic_bytes_per_launch = {ab}", f"traffic_over_algorithmic = {(fb + wb) / ab:.3f}"]
+        t_us = timed_mean_us(key, workload)
+        if t_us and ab:
+            gbs = ab / (t_us * 1e-6) / 1e9
+            lines += [f"# against MI355X peaks, with the kernel's mean duration in kernels_{workload}_kernel_stats.txt",
+                      f"mean_duration_us = {t_us:.2f}",
+                      f"algorithmic_GBps = {gbs:.1f}", f"algorithmic_frac_of_hbm_peak = {gbs / PEAK_HBM_GBS:.4f}"]
+            if c.get("FETCH_SIZE") is not None and c.get("WRITE_SIZE") is not None and fc and wc:
+                tb = c["FETCH_SIZE"] * 1024.0 * fc + c["WRITE_SIZE"] * 1024.0 * wc
+                lines.append(f"traffic_GBps = {tb / (t_us * 1e-6) / 1e9:.1f}")
+            kf = kernel_flops(wl).get(key)
+            if kf:
+                peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+                tf = kf / (t_us * 1e-6) / 1e12
+                lines += [f"algorithmic_flops_per_launch_kernel = {kf}", f"algorithmic_TFLOPs = {tf:.1f}",
+                          f"algorithmic_frac_of_mfma_peak = {tf / peak:.4f}"]
         if c.get("SQ_INSTS_MFMA") == 0:
             lines.append("# no MFMA instructions: this kernel computes on the vector ALUs")
         elif c.get("SQ_INSTS_MFMA") is not None:
