@@ -293,7 +293,10 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
  * h_in rounds once to dtype before its product with C (fp32 accumulation).
  * Outputs must not overlap the inputs or each other (final_state ==
  * shard_final excepted).  Same shape limits, alignment rules and errors as
- * ssd_chunk_scan_fwd; no workspace; T = 0 gives final = F + h_in. */
+ * ssd_chunk_scan_fwd, and SSD_ERR_UNSUPPORTED unless 64*nheads*headdim and
+ * 64*ngroups*dstate elements of dtype, and seqlen*nheads*4 bytes, stay below
+ * 2^31 bytes (32-bit offsets within a 64-token block and within dt); no
+ * workspace; T = 0 gives final = F + h_in. */
 ssd_status ssd_state_correction(void *y, const float *dt, const float *A, const void *C,
                                 const float *h_in, const float *shard_final, float *final_state,
                                 const int32_t *state_out_idx, float *state_out,

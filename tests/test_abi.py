@@ -366,3 +366,8 @@ def test_correction_binding_refuses_mis_sized_tensors():
         ssd.ssd_state_correction(y, dt, A, C.float(), torch.zeros(1, 2, 16, 16))  # C of another dtype
     with pytest.raises(ValueError):
         ssd.ssd_state_correction(y, dt, A, C, torch.zeros(1, 2, 16, 16))          # CPU tensors
+
+
+def test_correction_offset_limit():
+    # A sequence's dt must stay below 2^31 bytes (here 600000 * 1024 * 4).
+    assert CorrArgs(shape(T=600000, H=1024, G=2)).call() == ERR_UNSUPPORTED
